@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for Multi-Segment Attention -- test infrastructure only.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this package.  It shares no code with the HIP path.
+"""
+from .msa_oracle import attend, gather_context, masked_softmax_attention, merge_partials
+
+__all__ = ["attend", "gather_context", "masked_softmax_attention", "merge_partials"]
