@@ -1,0 +1,215 @@
+"""Multi-Segment Attention (MSA) for AMD MI355X (gfx950): Python binding of libmsa.
+
+This module only marshals arguments into the C ABI declared in
+``include/msa.h``; every step of the attention runs in the library's HIP
+kernels.  PyTorch tensors are accepted for device memory and the current HIP
+stream is used by default.  There is no fallback: if ``libmsa.so`` is missing
+or fails to load, importing the binding's entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "MsaError", "Pool", "SegDesc", "forward", "plan_debug", "library_path", "load_library",
+    "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
+    "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE",
+    "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS",
+]
+
+BF16, FP32 = 0, 1
+SEG_FRESH = 1
+BLOCK_SIZE = 16
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS = 1, 2, 3
+KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE = 0, 1, 2, 3
+
+EXPORTED_SYMBOLS = (
+    "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_last_error",
+    "msa_pool_set_option", "msa_pool_kernel_time", "msa_plan_debug",
+)
+
+_ERR_NAMES = {ERR_INVALID_ARG: "INVALID_ARG", ERR_UNSUPPORTED: "UNSUPPORTED", ERR_OOM: "OOM",
+              ERR_WORKSPACE: "WORKSPACE", ERR_HIP: "HIP"}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"MSA_ERR_{_ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+# ---- C structures (must match include/msa.h) ---------------------------------
+class _PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("device", ctypes.c_int32)]
+
+
+class _SegDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("q_offsets", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("seg_offsets", ctypes.c_void_p), ("segs", ctypes.c_void_p),
+                ("block_table_len", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("causal", ctypes.c_int32)]
+
+
+PLAN_ITEM_DTYPE = np.dtype([("kind", "<i4"), ("seq", "<i4"), ("kv_head", "<i4"), ("q_row0", "<i4"),
+                            ("n_q", "<i4"), ("blk_begin", "<i4"), ("blk_end", "<i4"), ("part_row", "<i4")])
+PLAN_BLOCK_DTYPE = np.dtype([("bt_index", "<i4"), ("pos0", "<i4"), ("valid", "<i4")])
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+
+
+def load_library():
+    """Load libmsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m kv_cache_attention_msa_amd.csrc.build)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.msa_create_pool.argtypes = [ctypes.POINTER(_PoolDesc), P, P, ctypes.POINTER(P)]
+    lib.msa_pool_kv_ptrs.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P)]
+    lib.msa_destroy_pool.argtypes = [P]
+    lib.msa_forward.argtypes = [P, ctypes.POINTER(_SegDesc), P, P, P, P, P]
+    lib.msa_last_error.argtypes = []
+    lib.msa_last_error.restype = ctypes.c_char_p
+    lib.msa_pool_set_option.argtypes = [P, I32, I64]
+    lib.msa_pool_kernel_time.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
+    lib.msa_plan_debug.argtypes = [ctypes.POINTER(_SegDesc), I32, I32, I32, I32, I32, P, I32,
+                                   ctypes.POINTER(I32), P, I32, ctypes.POINTER(I32)]
+    for name in EXPORTED_SYMBOLS:
+        if name != "msa_last_error":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MsaError(rc, load_library().msa_last_error().decode())
+
+
+def _ptr(x) -> int:
+    """Device/host address of a torch tensor, numpy array, or an int."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return int(x.data_ptr())
+
+
+def _current_stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else int(stream.cuda_stream)
+    import torch
+    if torch.cuda.is_available():
+        return int(torch.cuda.current_stream().cuda_stream)
+    return 0
+
+
+class SegDesc:
+    """Host-side segment descriptors for one msa_forward call (see msa_seg_desc)."""
+
+    def __init__(self, q_offsets, q_pos, seg_offsets, segs, block_table_len, num_q_heads,
+                 scale: float = 0.0, causal: bool = True):
+        self.q_offsets = np.ascontiguousarray(q_offsets, dtype=np.int32)
+        self.q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+        self.seg_offsets = np.ascontiguousarray(seg_offsets, dtype=np.int32)
+        self.segs = np.ascontiguousarray(np.asarray(segs, dtype=np.int32).reshape(-1, 4))
+        self.c = _SegDesc(len(self.q_offsets) - 1, int(num_q_heads),
+                          self.q_offsets.ctypes.data, self.q_pos.ctypes.data,
+                          self.seg_offsets.ctypes.data, self.segs.ctypes.data,
+                          int(block_table_len), float(scale), int(bool(causal)))
+
+    @classmethod
+    def from_workload(cls, wl):
+        return cls(wl.q_offsets, wl.q_pos, wl.seg_offsets, wl.segs, len(wl.block_table),
+                   wl.num_q_heads, wl.scale, bool(wl.causal))
+
+
+class Pool:
+    """A block-paged KV pool: K and V of shape [num_blocks, num_kv_heads, 16, head_dim].
+
+    Pass torch tensors ``k`` and ``v`` to wrap caller memory, or neither to let
+    the library allocate the pool.
+    """
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype=BF16, k=None, v=None, device=0):
+        lib = load_library()
+        if (k is None) != (v is None):
+            raise ValueError("give both k and v, or neither")
+        if k is not None:
+            for t in (k, v):
+                if not t.is_contiguous() or tuple(t.shape) != (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim):
+                    raise ValueError("k/v must be contiguous [num_blocks, num_kv_heads, 16, head_dim]")
+            device = k.device.index or 0
+        self._keep = (k, v)
+        self.desc = _PoolDesc(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, dtype, device)
+        h = ctypes.c_void_p()
+        _check(lib.msa_create_pool(ctypes.byref(self.desc), _ptr(k), _ptr(v), ctypes.byref(h)))
+        self.handle = h
+        self.num_blocks, self.num_kv_heads, self.head_dim, self.dtype = num_blocks, num_kv_heads, head_dim, dtype
+
+    def kv_ptrs(self):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(load_library().msa_pool_kv_ptrs(self.handle, ctypes.byref(k), ctypes.byref(v)))
+        return k.value, v.value
+
+    def set_option(self, option: int, value: int):
+        _check(load_library().msa_pool_set_option(self.handle, option, int(value)))
+
+    def kernel_time(self, kind: int, reset: bool = False):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(load_library().msa_pool_kernel_time(self.handle, kind, ctypes.byref(ms), ctypes.byref(n), int(reset)))
+        return ms.value, n.value
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            _check(load_library().msa_destroy_pool(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def forward(q, seg_desc: SegDesc, block_table, pool: Pool, out, lse=None, stream=None):
+    """Enqueue MSA for one batch on ``stream`` (default: torch's current stream).
+
+    ``q``/``out``: [total_q, num_q_heads, head_dim] device tensors of the pool
+    dtype; ``block_table``: int32 device tensor; ``lse``: float32
+    [total_q, num_q_heads] device tensor or None.
+    """
+    _check(load_library().msa_forward(_ptr(q), ctypes.byref(seg_desc.c), _ptr(block_table), pool.handle,
+                                      _ptr(out), _ptr(lse), _current_stream(stream)))
+
+
+def plan_debug(seg_desc: SegDesc, num_kv_heads: int, head_dim: int, dtype: int = BF16,
+               num_cus: int = 256, split_blocks: int = 0):
+    """Run the host planner alone; returns (items, blocks) as numpy structured arrays."""
+    lib = load_library()
+    ni, nb = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.msa_plan_debug(ctypes.byref(seg_desc.c), num_kv_heads, head_dim, dtype, num_cus, split_blocks,
+                              None, 0, ctypes.byref(ni), None, 0, ctypes.byref(nb)))
+    items = np.zeros(ni.value, dtype=PLAN_ITEM_DTYPE)
+    blocks = np.zeros(nb.value, dtype=PLAN_BLOCK_DTYPE)
+    _check(lib.msa_plan_debug(ctypes.byref(seg_desc.c), num_kv_heads, head_dim, dtype, num_cus, split_blocks,
+                              items.ctypes.data, len(items), ctypes.byref(ni),
+                              blocks.ctypes.data, len(blocks), ctypes.byref(nb)))
+    return items, blocks

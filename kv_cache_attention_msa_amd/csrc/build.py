@@ -1,0 +1,70 @@
+"""Build libmsa.so (host runtime + gfx950 kernels) in-tree with hipcc.
+
+    python -m kv_cache_attention_msa_amd.csrc.build      # or build() from Python
+
+Every call compiles every source again (objects go to ``_build/`` at the
+repository root, the library to ``kv_cache_attention_msa_amd/libmsa.so``).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmsa.so")
+ARCH = "gfx950"
+
+HOST_SOURCES = ["msa_plan.cpp", "msa_api.cpp"]
+HIP_SOURCES = sorted(f for f in os.listdir(HERE) if f.endswith(".hip"))
+
+COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{HERE}", "-Wall", "-Wno-unused-function"]
+# Packed fp32 ops stay off: the kernels are written for scalar fp32 VALU math.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fno-gpu-rdc"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + p.stdout)
+    return p.stdout
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    cmds, objs = [], []
+    for src in HOST_SOURCES + HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        extra = DEVICE + ["-x", "hip"] if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"]
+        cmds.append([cc, "-c"] + COMMON + extra + [os.path.join(HERE, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        outs = list(ex.map(_run, cmds))
+    if verbose:
+        for c, o in zip(cmds, outs):
+            print(" ".join(c))
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,463 @@
+// C ABI of libmsa: pool lifetime, per-call plan upload and kernel launches.
+//
+// One msa_forward call:
+//   1. checks every argument and builds the plan on the host (no HIP call
+//      before this succeeds, so an error leaves the stream untouched);
+//   2. packs the plan (block list, query positions, work and merge items) into
+//      one of two pinned staging buffers and enqueues a single host-to-device
+//      copy into the pool's workspace on the caller's stream;
+//   3. enqueues the prefill, decode and fp32 kernels for the items of each
+//      kind, then the merge kernel when some tile was split over KV.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "msa_internal.h"
+
+using namespace msa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(MSA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+#define MSA_HIP(call)                                         \
+  do {                                                        \
+    hipError_t e_ = (call);                                   \
+    if (e_ != hipSuccess) return hip_error(e_, #call);        \
+  } while (0)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Restores the calling thread's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && (prev == dev || hipSetDevice(dev) == hipSuccess)) ok = true;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+struct TimingRecord {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct msa_pool {
+  msa_pool_desc desc{};
+  void* k = nullptr;
+  void* v = nullptr;
+  bool owns_kv = false;
+  int num_cus = 0;  // 0: not queried yet
+
+  // options
+  bool timing = false;
+  int32_t split_blocks = 0;
+  int32_t num_cus_override = 0;
+
+  // device workspace: [plan upload area | partial O | partial lse]
+  void* d_ws = nullptr;
+  size_t ws_bytes = 0;
+  // pinned staging, two buffers used alternately
+  void* h_stage[2] = {nullptr, nullptr};
+  size_t stage_bytes[2] = {0, 0};
+  hipEvent_t stage_done[2] = {nullptr, nullptr};
+  bool stage_pending[2] = {false, false};
+  int stage_next = 0;
+  hipStream_t last_stream = nullptr;
+  bool used = false;
+
+  // timing
+  std::vector<TimingRecord> records;
+  std::vector<hipEvent_t> spare_events;
+  double total_ms[kNumKinds] = {0, 0, 0, 0};
+  int64_t launches[kNumKinds] = {0, 0, 0, 0};
+
+  Plan plan;
+};
+
+namespace {
+
+int take_event(msa_pool* p, hipEvent_t* ev) {
+  if (!p->spare_events.empty()) {
+    *ev = p->spare_events.back();
+    p->spare_events.pop_back();
+    return MSA_OK;
+  }
+  MSA_HIP(hipEventCreate(ev));
+  return MSA_OK;
+}
+
+int collect_timing(msa_pool* p) {
+  for (auto& r : p->records) {
+    MSA_HIP(hipEventSynchronize(r.stop));
+    float ms = 0.f;
+    MSA_HIP(hipEventElapsedTime(&ms, r.start, r.stop));
+    p->total_ms[r.kind] += ms;
+    p->launches[r.kind] += 1;
+    p->spare_events.push_back(r.start);
+    p->spare_events.push_back(r.stop);
+  }
+  p->records.clear();
+  return MSA_OK;
+}
+
+// Launch one kernel kind, bracketed by events when timing is on.
+template <typename F>
+int timed_launch(msa_pool* p, int kind, hipStream_t stream, F&& launch) {
+  TimingRecord rec{kind, nullptr, nullptr};
+  if (p->timing) {
+    int rc = take_event(p, &rec.start);
+    if (rc) return rc;
+    rc = take_event(p, &rec.stop);
+    if (rc) return rc;
+    MSA_HIP(hipEventRecord(rec.start, stream));
+  }
+  int e = launch();
+  if (e != hipSuccess) return hip_error((hipError_t)e, "kernel launch");
+  if (p->timing) {
+    MSA_HIP(hipEventRecord(rec.stop, stream));
+    p->records.push_back(rec);
+    if (p->records.size() > 4096) return collect_timing(p);
+  }
+  return MSA_OK;
+}
+
+int ensure_device_ws(msa_pool* p, size_t bytes, hipStream_t stream) {
+  if (bytes <= p->ws_bytes) return MSA_OK;
+  size_t want = std::max(bytes, p->ws_bytes + p->ws_bytes / 2);
+  want = align_up(want, size_t(1) << 20);
+  if (p->d_ws) {
+    // Work already enqueued may still read the old workspace.
+    if (p->used) MSA_HIP(hipStreamSynchronize(p->last_stream));
+    MSA_HIP(hipStreamSynchronize(stream));
+    MSA_HIP(hipFree(p->d_ws));
+    p->d_ws = nullptr;
+    p->ws_bytes = 0;
+  }
+  hipError_t e = hipMalloc(&p->d_ws, want);
+  if (e != hipSuccess) {
+    p->d_ws = nullptr;
+    (void)hipGetLastError();
+    return set_error(MSA_ERR_OOM, "workspace hipMalloc(%zu) failed: %s", want, hipGetErrorString(e));
+  }
+  p->ws_bytes = want;
+  return MSA_OK;
+}
+
+int ensure_stage(msa_pool* p, int slot, size_t bytes) {
+  if (!p->stage_done[slot]) MSA_HIP(hipEventCreateWithFlags(&p->stage_done[slot], hipEventDisableTiming));
+  if (p->stage_pending[slot]) {
+    // The copy that last read this buffer must have finished before we rewrite it.
+    MSA_HIP(hipEventSynchronize(p->stage_done[slot]));
+    p->stage_pending[slot] = false;
+  }
+  if (bytes <= p->stage_bytes[slot]) return MSA_OK;
+  size_t want = align_up(std::max(bytes, p->stage_bytes[slot] * 3 / 2), size_t(1) << 16);
+  if (p->h_stage[slot]) {
+    MSA_HIP(hipHostFree(p->h_stage[slot]));
+    p->h_stage[slot] = nullptr;
+    p->stage_bytes[slot] = 0;
+  }
+  hipError_t e = hipHostMalloc(&p->h_stage[slot], want, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    p->h_stage[slot] = nullptr;
+    (void)hipGetLastError();
+    return set_error(MSA_ERR_OOM, "pinned hipHostMalloc(%zu) failed: %s", want, hipGetErrorString(e));
+  }
+  p->stage_bytes[slot] = want;
+  return MSA_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == MSA_FP32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+int msa_create_pool(const msa_pool_desc* desc, void* k_base, void* v_base, msa_pool** out) {
+  if (!desc || !out) return set_error(MSA_ERR_INVALID_ARG, "desc or out is NULL");
+  *out = nullptr;
+  if (desc->num_blocks <= 0 || desc->num_kv_heads <= 0)
+    return set_error(MSA_ERR_INVALID_ARG, "num_blocks and num_kv_heads must be > 0");
+  if (desc->block_size != MSA_BLOCK_SIZE)
+    return set_error(MSA_ERR_UNSUPPORTED, "block_size %d is not supported (16)", desc->block_size);
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return set_error(MSA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", desc->head_dim);
+  if (desc->dtype != MSA_BF16 && desc->dtype != MSA_FP32)
+    return set_error(MSA_ERR_UNSUPPORTED, "dtype %d is not supported", desc->dtype);
+  if (desc->device < 0) return set_error(MSA_ERR_INVALID_ARG, "device %d < 0", desc->device);
+  if ((k_base == nullptr) != (v_base == nullptr))
+    return set_error(MSA_ERR_INVALID_ARG, "give both k_base and v_base, or neither");
+  msa_pool* p = new (std::nothrow) msa_pool();
+  if (!p) return set_error(MSA_ERR_OOM, "host allocation failed");
+  p->desc = *desc;
+  if (k_base) {
+    p->k = k_base;
+    p->v = v_base;
+  } else {
+    DeviceGuard g(desc->device);
+    if (!g.ok) {
+      delete p;
+      return set_error(MSA_ERR_HIP, "cannot select device %d", desc->device);
+    }
+    const size_t bytes = (size_t)desc->num_blocks * desc->num_kv_heads * MSA_BLOCK_SIZE *
+                         desc->head_dim * elem_size(desc->dtype);
+    if (hipMalloc(&p->k, bytes) != hipSuccess || hipMalloc(&p->v, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      if (p->k) (void)hipFree(p->k);
+      delete p;
+      return set_error(MSA_ERR_OOM, "pool hipMalloc of 2 x %zu bytes failed", bytes);
+    }
+    p->owns_kv = true;
+  }
+  *out = p;
+  return MSA_OK;
+}
+
+int msa_pool_kv_ptrs(const msa_pool* pool, void** k, void** v) {
+  if (!pool || !k || !v) return set_error(MSA_ERR_INVALID_ARG, "NULL argument");
+  *k = pool->k;
+  *v = pool->v;
+  return MSA_OK;
+}
+
+int msa_destroy_pool(msa_pool* p) {
+  if (!p) return MSA_OK;
+  int rc = MSA_OK;
+  const bool touched = p->used || p->owns_kv || p->d_ws || p->h_stage[0] || p->h_stage[1];
+  if (touched) {
+    DeviceGuard g(p->desc.device);
+    if (p->used && hipStreamSynchronize(p->last_stream) != hipSuccess) rc = MSA_ERR_HIP;
+    for (auto& r : p->records) {
+      (void)hipEventDestroy(r.start);
+      (void)hipEventDestroy(r.stop);
+    }
+    for (auto e : p->spare_events) (void)hipEventDestroy(e);
+    for (int s = 0; s < 2; ++s) {
+      if (p->stage_done[s]) (void)hipEventDestroy(p->stage_done[s]);
+      if (p->h_stage[s]) (void)hipHostFree(p->h_stage[s]);
+    }
+    if (p->d_ws) (void)hipFree(p->d_ws);
+    if (p->owns_kv) {
+      (void)hipFree(p->k);
+      (void)hipFree(p->v);
+    }
+  }
+  delete p;
+  if (rc) return set_error(rc, "stream synchronisation failed while destroying the pool");
+  return MSA_OK;
+}
+
+int msa_pool_set_option(msa_pool* p, int32_t option, int64_t value) {
+  if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
+  switch (option) {
+    case MSA_OPT_TIMING: p->timing = value != 0; return MSA_OK;
+    case MSA_OPT_SPLIT_BLOCKS:
+      if (value < 0 || value > (1 << 30)) return set_error(MSA_ERR_INVALID_ARG, "bad split_blocks");
+      p->split_blocks = (int32_t)value;
+      return MSA_OK;
+    case MSA_OPT_NUM_CUS:
+      if (value < 0 || value > 65536) return set_error(MSA_ERR_INVALID_ARG, "bad num_cus");
+      p->num_cus_override = (int32_t)value;
+      return MSA_OK;
+    default: return set_error(MSA_ERR_INVALID_ARG, "unknown option %d", option);
+  }
+}
+
+int msa_pool_kernel_time(msa_pool* p, int32_t kind, double* total_ms, int64_t* launches, int32_t reset) {
+  if (!p || !total_ms || !launches) return set_error(MSA_ERR_INVALID_ARG, "NULL argument");
+  if (kind < 0 || kind >= kNumKinds) return set_error(MSA_ERR_INVALID_ARG, "bad kernel kind %d", kind);
+  if (!p->records.empty()) {
+    DeviceGuard g(p->desc.device);
+    int rc = collect_timing(p);
+    if (rc) return rc;
+  }
+  *total_ms = p->total_ms[kind];
+  *launches = p->launches[kind];
+  if (reset) {
+    for (int k = 0; k < kNumKinds; ++k) {
+      p->total_ms[k] = 0;
+      p->launches[k] = 0;
+    }
+  }
+  return MSA_OK;
+}
+
+int msa_plan_debug(const msa_seg_desc* desc, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   int32_t num_cus, int32_t split_blocks, msa_plan_item* items, int32_t max_items,
+                   int32_t* n_items, msa_plan_block* blocks, int32_t max_blocks, int32_t* n_blocks) {
+  if (!n_items || !n_blocks) return set_error(MSA_ERR_INVALID_ARG, "n_items or n_blocks is NULL");
+  if ((max_items > 0 && !items) || (max_blocks > 0 && !blocks))
+    return set_error(MSA_ERR_INVALID_ARG, "NULL output array");
+  PlanConfig cfg;
+  cfg.num_kv_heads = num_kv_heads;
+  cfg.head_dim = head_dim;
+  cfg.dtype = dtype;
+  cfg.num_cus = num_cus > 0 ? num_cus : 256;
+  cfg.split_blocks = split_blocks;
+  Plan plan;
+  std::string err;
+  int rc = build_plan(desc, cfg, plan, err);
+  if (rc) return set_error(rc, "%s", err.c_str());
+  int32_t n = 0;
+  for (int k = 0; k < 3; ++k)
+    for (const WorkItem& w : plan.items[k]) {
+      if (n < max_items)
+        items[n] = msa_plan_item{k, w.seq, w.kv_head, w.q_row0, w.n_q, w.blk_begin, w.blk_end, w.part_row};
+      ++n;
+    }
+  *n_items = n;
+  const int32_t nb = (int32_t)plan.blocks.size();
+  for (int32_t i = 0; i < std::min(nb, max_blocks); ++i) {
+    const uint32_t bv = (uint32_t)plan.blocks[i].bt_valid;
+    blocks[i] = msa_plan_block{(int32_t)(bv & ((1u << kBtIndexBits) - 1)), plan.blocks[i].pos0,
+                               (int32_t)(bv >> kBtIndexBits) + 1};
+  }
+  *n_blocks = nb;
+  return MSA_OK;
+}
+
+int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_table, msa_pool* p,
+                void* out, float* lse, void* stream_) {
+  // ---- host-side checks and planning (no HIP call before they pass) ----
+  if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
+  if (!desc) return set_error(MSA_ERR_INVALID_ARG, "seg_desc is NULL");
+  PlanConfig cfg;
+  cfg.num_kv_heads = p->desc.num_kv_heads;
+  cfg.head_dim = p->desc.head_dim;
+  cfg.dtype = p->desc.dtype;
+  cfg.num_cus = p->num_cus_override > 0 ? p->num_cus_override : (p->num_cus > 0 ? p->num_cus : 256);
+  cfg.split_blocks = p->split_blocks;
+  std::string err;
+  int rc = build_plan(desc, cfg, p->plan, err);
+  if (rc) return set_error(rc, "%s", err.c_str());
+  Plan& plan = p->plan;
+  if (plan.total_q > 0 && (!q || !out)) return set_error(MSA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!plan.blocks.empty() && !block_table) return set_error(MSA_ERR_INVALID_ARG, "block_table is NULL");
+  if (plan.total_q > 0 && (q == out || (const void*)lse == q || (void*)lse == out))
+    return set_error(MSA_ERR_INVALID_ARG, "q, out and lse must not alias");
+  if (plan.total_q == 0) return MSA_OK;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  DeviceGuard guard(p->desc.device);
+  if (!guard.ok) return set_error(MSA_ERR_HIP, "cannot select device %d", p->desc.device);
+  if (p->num_cus == 0) {
+    int n = 0;
+    MSA_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, p->desc.device));
+    p->num_cus = n > 0 ? n : 256;
+    if (p->num_cus_override == 0 && p->num_cus != cfg.num_cus) {
+      cfg.num_cus = p->num_cus;
+      rc = build_plan(desc, cfg, plan, err);
+      if (rc) return set_error(rc, "%s", err.c_str());
+    }
+  }
+
+  // ---- pack the plan ----
+  const int D = p->desc.head_dim;
+  size_t off = 0;
+  const size_t off_blocks = off;
+  off = align_up(off + plan.blocks.size() * sizeof(BlockEntry), 256);
+  const size_t off_qpos = off;
+  off = align_up(off + plan.q_pos.size() * sizeof(int32_t), 256);
+  size_t off_items[3];
+  for (int k = 0; k < 3; ++k) {
+    off_items[k] = off;
+    off = align_up(off + plan.items[k].size() * sizeof(WorkItem), 256);
+  }
+  const size_t off_merge = off;
+  off = align_up(off + plan.merges.size() * sizeof(MergeItem), 256);
+  const size_t plan_bytes = off;
+  const size_t off_part_o = plan_bytes;
+  const size_t off_part_lse = align_up(off_part_o + (size_t)plan.part_rows * D * sizeof(float), 256);
+  const size_t ws_need = align_up(off_part_lse + (size_t)plan.part_rows * sizeof(float), 256);
+
+  rc = ensure_device_ws(p, ws_need, stream);
+  if (rc) return rc;
+  const int slot = p->stage_next;
+  p->stage_next ^= 1;
+  rc = ensure_stage(p, slot, plan_bytes);
+  if (rc) return rc;
+  char* h = (char*)p->h_stage[slot];
+  if (!plan.blocks.empty()) memcpy(h + off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
+  memcpy(h + off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
+  for (int k = 0; k < 3; ++k)
+    if (!plan.items[k].empty())
+      memcpy(h + off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
+  if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
+
+  char* dws = (char*)p->d_ws;
+  MSA_HIP(hipMemcpyAsync(dws, h, plan_bytes, hipMemcpyHostToDevice, stream));
+  MSA_HIP(hipEventRecord(p->stage_done[slot], stream));
+  p->stage_pending[slot] = true;
+  p->used = true;
+  p->last_stream = stream;
+
+  // ---- launches ----
+  KernelArgs a{};
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.k = p->k;
+  a.v = p->v;
+  a.block_table = block_table;
+  a.blocks = (const BlockEntry*)(dws + off_blocks);
+  a.q_pos = (const int32_t*)(dws + off_qpos);
+  a.merges = (const MergeItem*)(dws + off_merge);
+  a.n_merges = (int32_t)plan.merges.size();
+  a.part_o = (float*)(dws + off_part_o);
+  a.part_lse = (float*)(dws + off_part_lse);
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = p->desc.num_kv_heads;
+  a.group = desc->num_q_heads / p->desc.num_kv_heads;
+  a.causal = desc->causal;
+  const float scale = desc->scale != 0.f ? desc->scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  for (int k = 0; k < 3; ++k) {
+    if (plan.items[k].empty()) continue;
+    a.items = (const WorkItem*)(dws + off_items[k]);
+    a.n_items = (int32_t)plan.items[k].size();
+    rc = timed_launch(p, k, stream, [&]() {
+      if (k == kPrefill) return launch_prefill(a, D, stream);
+      if (k == kDecode) return launch_decode(a, D, stream);
+      return launch_fp32(a, D, stream);
+    });
+    if (rc) return rc;
+  }
+  if (!plan.merges.empty()) {
+    a.items = nullptr;
+    a.n_items = 0;
+    rc = timed_launch(p, kMerge, stream, [&]() { return launch_merge(a, D, p->desc.dtype, stream); });
+    if (rc) return rc;
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

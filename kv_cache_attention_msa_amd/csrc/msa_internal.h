@@ -1,0 +1,104 @@
+// Internal types shared by the host runtime (planner, pool) and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "msa.h"
+
+namespace msa {
+
+constexpr int kBlock = MSA_BLOCK_SIZE;
+constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per prefill tile
+constexpr int kDecodeMRows = 16;     // pairs per decode tile (one MFMA column block)
+constexpr int kFp32MRows = 64;       // pairs per fp32 tile
+constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accepted
+constexpr int kBtIndexBits = 28;     // block-table index bits in BlockEntry::bt_valid
+
+// One entry of a sequence's position-ordered block list (8 bytes on device).
+struct BlockEntry {
+  int32_t bt_valid;  // bits 0..27: index into block_table; bits 28..31: valid slots - 1
+  int32_t pos0;      // absolute position of slot 0
+};
+
+// One unit of kernel work: a tile of query rows of one sequence and one kv
+// head, against a contiguous range of that sequence's block list.
+struct WorkItem {
+  int32_t kv_head;
+  int32_t q_row0;    // first query row (global row index)
+  int32_t n_q;       // query rows in the tile
+  int32_t blk_begin; // [blk_begin, blk_end) into the block list
+  int32_t blk_end;
+  int32_t part_row;  // -1: final output; else first row of this split's partials
+  int32_t seq;
+  int32_t pad;
+};
+
+// Rows of one tile that was split over KV: n_splits partials of n_mrows rows
+// each, stored back to back from part_row0.
+struct MergeItem {
+  int32_t kv_head;
+  int32_t q_row0;
+  int32_t n_q;
+  int32_t part_row0;
+  int32_t n_splits;
+  int32_t n_mrows;
+  int32_t pad0, pad1;
+};
+
+enum Kind { kPrefill = MSA_KERNEL_PREFILL, kDecode = MSA_KERNEL_DECODE,
+            kFp32 = MSA_KERNEL_FP32, kMerge = MSA_KERNEL_MERGE, kNumKinds = 4 };
+
+struct Plan {
+  std::vector<BlockEntry> blocks;
+  std::vector<int32_t> q_pos;
+  std::vector<WorkItem> items[3];   // per kernel kind (prefill, decode, fp32)
+  std::vector<MergeItem> merges;
+  int64_t part_rows = 0;            // partial rows (each head_dim floats + 1 lse)
+  int32_t total_q = 0;
+};
+
+struct PlanConfig {
+  int32_t num_kv_heads = 0;
+  int32_t head_dim = 0;
+  int32_t dtype = MSA_BF16;
+  int32_t num_cus = 256;
+  int32_t split_blocks = 0;         // >0 forces this cap on blocks per item
+};
+
+// Checks every argument of the descriptor and builds the plan.  Host only;
+// returns an MSA_* status and fills `err` on failure.
+int build_plan(const msa_seg_desc* desc, const PlanConfig& cfg, Plan& plan, std::string& err);
+
+// Kernel launch parameters (identical for every kernel kind).
+struct KernelArgs {
+  const void* q;
+  void* out;
+  float* lse;             // may be null
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const BlockEntry* blocks;
+  const int32_t* q_pos;
+  const WorkItem* items;
+  const MergeItem* merges;
+  float* part_o;          // [part_rows][head_dim]
+  float* part_lse;        // [part_rows]
+  int32_t n_items;
+  int32_t n_merges;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // num_q_heads / num_kv_heads
+  int32_t causal;
+  float scale_log2;       // scale * log2(e)
+};
+
+// Launchers (msa_kernels.hip).  Return a hipError_t value.
+int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
+int launch_decode(const KernelArgs& a, int head_dim, void* stream);
+int launch_fp32(const KernelArgs& a, int head_dim, void* stream);
+int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream);
+
+}  // namespace msa

@@ -1,0 +1,217 @@
+// Argument checks and the split-KV work planner (host only, no HIP calls).
+//
+// The planner turns the caller's segment descriptors into
+//  * a position-ordered block list per sequence (segments sorted by position,
+//    expanded to one entry per KV block, so a 64-key kernel tile may span a
+//    segment boundary and only the partially filled last block of a segment
+//    wastes slots);
+//  * work items: a tile of query rows of one sequence and one kv head against
+//    the prefix of that sequence's block list that the tile can see (causal by
+//    absolute position: a block is needed iff its first position <= the tile's
+//    largest query position), cut into KV splits when the device would
+//    otherwise be unevenly loaded, largest first;
+//  * merge items for every tile that was split.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <limits>
+#include <numeric>
+
+#include "msa_internal.h"
+
+namespace msa {
+
+static int fail(std::string& err, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  err = buf;
+  return code;
+}
+
+namespace {
+
+struct Tile {
+  int32_t kind, seq, kv_head, q_row0, n_q, blk_begin, blk_end;
+};
+
+// Largest block-count of one work item before the planner splits a tile.
+int64_t auto_chunk(int kind, int64_t total_blocks, int num_cus) {
+  // Resident work-groups the planner balances for, per compute unit.
+  const int64_t slots_per_cu = (kind == kPrefill) ? 2 : 4;
+  const int64_t min_chunk = (kind == kPrefill) ? 16 : (kind == kDecode ? 32 : 4);
+  const int64_t slots = std::max<int64_t>(1, slots_per_cu * num_cus);
+  return std::max<int64_t>(min_chunk, (total_blocks + slots - 1) / slots);
+}
+
+}  // namespace
+
+int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::string& err) {
+  const int INV = MSA_ERR_INVALID_ARG, UNS = MSA_ERR_UNSUPPORTED;
+  plan.blocks.clear();
+  plan.q_pos.clear();
+  for (auto& v : plan.items) v.clear();
+  plan.merges.clear();
+  plan.part_rows = 0;
+  plan.total_q = 0;
+
+  if (!d) return fail(err, INV, "seg_desc is NULL");
+  if (cfg.head_dim != 64 && cfg.head_dim != 128)
+    return fail(err, UNS, "head_dim %d is not supported (64 or 128)", cfg.head_dim);
+  if (cfg.dtype != MSA_BF16 && cfg.dtype != MSA_FP32)
+    return fail(err, UNS, "dtype %d is not supported", cfg.dtype);
+  if (cfg.num_kv_heads <= 0) return fail(err, INV, "num_kv_heads must be > 0");
+  if (d->batch < 0) return fail(err, INV, "batch %d < 0", d->batch);
+  if (d->num_q_heads <= 0) return fail(err, INV, "num_q_heads %d <= 0", d->num_q_heads);
+  if (d->num_q_heads % cfg.num_kv_heads != 0)
+    return fail(err, INV, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                cfg.num_kv_heads);
+  const int group = d->num_q_heads / cfg.num_kv_heads;
+  if (group > kMaxGroup) return fail(err, UNS, "GQA ratio %d exceeds %d", group, kMaxGroup);
+  if (d->causal != 0 && d->causal != 1) return fail(err, INV, "causal must be 0 or 1");
+  if (!std::isfinite(d->scale)) return fail(err, INV, "scale is not finite");
+  if (d->block_table_len < 0) return fail(err, INV, "block_table_len < 0");
+  if (d->block_table_len > (1 << kBtIndexBits))
+    return fail(err, MSA_ERR_WORKSPACE, "block_table_len %d exceeds 2^%d", d->block_table_len,
+                kBtIndexBits);
+  const int B = d->batch;
+  if (B == 0) return MSA_OK;
+  if (!d->q_offsets || !d->seg_offsets) return fail(err, INV, "q_offsets or seg_offsets is NULL");
+  if (d->q_offsets[0] != 0 || d->seg_offsets[0] != 0)
+    return fail(err, INV, "q_offsets[0] and seg_offsets[0] must be 0");
+  for (int b = 0; b < B; ++b) {
+    if (d->q_offsets[b + 1] < d->q_offsets[b])
+      return fail(err, INV, "q_offsets decreases at sequence %d", b);
+    if (d->seg_offsets[b + 1] < d->seg_offsets[b])
+      return fail(err, INV, "seg_offsets decreases at sequence %d", b);
+  }
+  const int32_t total_q = d->q_offsets[B];
+  const int32_t total_segs = d->seg_offsets[B];
+  if ((int64_t)total_q * d->num_q_heads > std::numeric_limits<int32_t>::max())
+    return fail(err, MSA_ERR_WORKSPACE, "total_q * num_q_heads exceeds 2^31");
+  if (total_q > 0 && !d->q_pos) return fail(err, INV, "q_pos is NULL");
+  if (total_segs > 0 && !d->segs) return fail(err, INV, "segs is NULL");
+  plan.total_q = total_q;
+
+  std::vector<Tile> tiles;
+  std::vector<int32_t> order;
+  for (int b = 0; b < B; ++b) {
+    const int32_t s0 = d->seg_offsets[b], s1 = d->seg_offsets[b + 1];
+    order.clear();
+    for (int32_t s = s0; s < s1; ++s) {
+      const msa_segment& sg = d->segs[s];
+      if (sg.len < 0 || sg.pos_start < 0 || sg.bt_start < 0)
+        return fail(err, INV, "segment %d: negative pos_start, len or bt_start", s);
+      if ((int64_t)sg.pos_start + sg.len > std::numeric_limits<int32_t>::max())
+        return fail(err, INV, "segment %d: pos_start + len overflows int32", s);
+      const int64_t nblk = (sg.len + kBlock - 1) / kBlock;
+      if ((int64_t)sg.bt_start + nblk > d->block_table_len)
+        return fail(err, INV, "segment %d: blocks [%d, %lld) exceed block_table_len %d", s,
+                    sg.bt_start, (long long)(sg.bt_start + nblk), d->block_table_len);
+      if (sg.len > 0) order.push_back(s);
+    }
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return d->segs[x].pos_start < d->segs[y].pos_start;
+    });
+    for (size_t i = 1; i < order.size(); ++i) {
+      const msa_segment& p = d->segs[order[i - 1]];
+      const msa_segment& c = d->segs[order[i]];
+      if ((int64_t)p.pos_start + p.len > c.pos_start)
+        return fail(err, INV, "sequence %d: segments %d and %d overlap in position", b,
+                    order[i - 1], order[i]);
+    }
+    const int32_t seq_blk0 = (int32_t)plan.blocks.size();
+    for (int32_t s : order) {
+      const msa_segment& sg = d->segs[s];
+      for (int32_t j = 0; j * kBlock < sg.len; ++j) {
+        const int32_t valid = std::min(kBlock, sg.len - j * kBlock);
+        BlockEntry e;
+        e.bt_valid = (int32_t)((uint32_t)(sg.bt_start + j) | ((uint32_t)(valid - 1) << kBtIndexBits));
+        e.pos0 = sg.pos_start + j * kBlock;
+        plan.blocks.push_back(e);
+      }
+    }
+    const int32_t seq_blk1 = (int32_t)plan.blocks.size();
+
+    // Query tiles of this sequence.
+    const int32_t q0 = d->q_offsets[b], q1 = d->q_offsets[b + 1];
+    const int32_t nq = q1 - q0;
+    if (nq == 0) continue;
+    int kind;
+    int32_t tile_rows;
+    if (cfg.dtype == MSA_FP32) {
+      kind = kFp32;
+      tile_rows = std::max(1, kFp32MRows / group);
+    } else if (group <= kDecodeMRows && (int64_t)nq * group <= kDecodeMRows) {
+      kind = kDecode;
+      tile_rows = nq;
+    } else {
+      kind = kPrefill;
+      tile_rows = kPrefillMRows / group;
+    }
+    for (int32_t r = q0; r < q1; r += tile_rows) {
+      const int32_t n = std::min(tile_rows, q1 - r);
+      int32_t end = seq_blk1;
+      if (d->causal) {
+        int32_t qmax = d->q_pos[r];
+        for (int32_t i = r + 1; i < r + n; ++i) qmax = std::max(qmax, d->q_pos[i]);
+        // first block whose slot-0 position is beyond every query of the tile
+        auto it = std::upper_bound(plan.blocks.begin() + seq_blk0, plan.blocks.begin() + seq_blk1,
+                                   qmax, [](int32_t v, const BlockEntry& e) { return v < e.pos0; });
+        end = (int32_t)(it - plan.blocks.begin());
+      }
+      tiles.push_back(Tile{kind, b, 0, r, n, seq_blk0, end});
+    }
+  }
+  plan.q_pos.assign(d->q_pos, d->q_pos + total_q);
+
+  // Expand tiles over kv heads and split long ones.
+  int64_t total_blocks[3] = {0, 0, 0};
+  for (const Tile& t : tiles) total_blocks[t.kind] += (int64_t)(t.blk_end - t.blk_begin) * cfg.num_kv_heads;
+  int64_t chunk[3];
+  for (int k = 0; k < 3; ++k)
+    chunk[k] = cfg.split_blocks > 0 ? cfg.split_blocks : auto_chunk(k, total_blocks[k], cfg.num_cus);
+
+  for (const Tile& t : tiles) {
+    const int32_t nblk = t.blk_end - t.blk_begin;
+    const int64_t c = chunk[t.kind];
+    int32_t nsplit = 1;
+    if (cfg.split_blocks > 0 ? nblk > c : nblk > c + c / 2)
+      nsplit = (int32_t)((nblk + c - 1) / c);
+    const int32_t align = (t.kind == kPrefill) ? 4 : 1;  // prefill consumes 4 blocks per step
+    nsplit = std::min(nsplit, (nblk + align - 1) / align);
+    if (nsplit < 1) nsplit = 1;
+    const int32_t n_mrows = t.n_q * group;
+    for (int32_t h = 0; h < cfg.num_kv_heads; ++h) {
+      if (nsplit == 1) {
+        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, 0});
+        continue;
+      }
+      if ((int64_t)plan.part_rows + (int64_t)nsplit * n_mrows > std::numeric_limits<int32_t>::max())
+        return fail(err, MSA_ERR_WORKSPACE, "split partials exceed 2^31 rows");
+      const int32_t part0 = (int32_t)plan.part_rows;
+      const int32_t units = (nblk + align - 1) / align;
+      int32_t done = 0;
+      for (int32_t s = 0; s < nsplit; ++s) {
+        const int32_t u1 = (int32_t)((int64_t)units * (s + 1) / nsplit);
+        const int32_t b1 = std::min(nblk, u1 * align);
+        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin + done,
+                                              t.blk_begin + b1, part0 + s * n_mrows, t.seq, 0});
+        done = b1;
+      }
+      plan.merges.push_back(MergeItem{h, t.q_row0, t.n_q, part0, nsplit, n_mrows, 0, 0});
+      plan.part_rows += (int64_t)nsplit * n_mrows;
+    }
+  }
+  // Largest work first, so the tail of the launch is made of small items.
+  for (auto& v : plan.items)
+    std::stable_sort(v.begin(), v.end(), [](const WorkItem& x, const WorkItem& y) {
+      return (x.blk_end - x.blk_begin) > (y.blk_end - y.blk_begin);
+    });
+  return MSA_OK;
+}
+
+}  // namespace msa

@@ -1,0 +1,145 @@
+"""GPU parity: libmsa (HIP, gfx950) against the fp64 oracle on the same seeded inputs.
+
+Bounds: fp32 inputs max-abs 1e-5; bf16 inputs max-abs 2e-2 and mean-abs 2e-3,
+applied to out and to lse.  Pools hold NaN in every slot outside the
+segments, so a read outside them shows up as a non-finite output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_attention_msa_amd as msa
+import workloads as W
+from msa_gpu_util import GpuCase, compare, oracle_result, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, split_blocks=0, rows=None):
+    print(f"[parity] {wl.name} split_blocks={split_blocks}", flush=True)
+    case = GpuCase(wl)
+    try:
+        out, lse = case.run(split_blocks)
+    finally:
+        case.close()
+    ref_out, ref_lse = oracle_result(wl, rows)
+    return compare(wl, out, lse, ref_out, ref_lse, rows)
+
+
+# ---- configuration 1 (fp32) ------------------------------------------------
+def test_config1_fp32():
+    _check(W.config1())
+
+
+def test_config1_fp32_split_and_merge():
+    _check(W.config1(), split_blocks=1)
+
+
+# ---- small bf16 cases ---------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_random_bf16(seed):
+    H = [(8, 2), (32, 8), (4, 4), (64, 8), (16, 1), (6, 2)][seed]
+    d = 64 if seed % 2 else 128
+    _check(W.random_case(seed, batch=4, H_q=H[0], H_kv=H[1], d=d))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_bf16_forced_split(seed):
+    _check(W.random_case(20 + seed, batch=3, H_q=8, H_kv=2, d=128, max_ctx=600), split_blocks=3)
+
+
+def test_random_fp32_cases():
+    for seed in range(3):
+        _check(W.random_case(40 + seed, batch=3, H_q=4, H_kv=2, d=64, dtype="fp32"))
+        _check(W.random_case(50 + seed, batch=2, H_q=2, H_kv=1, d=128, dtype="fp32"), split_blocks=2)
+
+
+def test_asymcache_layout():
+    """Eq. 5 layout: cached l1 | recomputed q1 (with queries) | cached suffix l2 | new q2 (with queries).
+    Rows of q1 must not see l2."""
+    l1, q1, l2, q2 = 300, 70, 200, 90
+    segs = [(0, l1), (l1, q1, W.SEG_FRESH), (l1 + q1, l2), (l1 + q1 + l2, q2, W.SEG_FRESH)]
+    qp = list(range(l1, l1 + q1)) + list(range(l1 + q1 + l2, l1 + q1 + l2 + q2))
+    for d in (64, 128):
+        _check(W.custom([(segs, qp)], H_q=32, H_kv=8, d=d, seed=5))
+
+
+def test_edge_cases():
+    cases = [
+        # length-1 segments, lengths not multiple of 16, a query before all keys
+        W.custom([([(5, 1), (7, 1), (20, 17), (50, 33)], [0, 6, 7, 30, 82])], H_q=8, H_kv=2, d=128, seed=1),
+        # sequence with no segments, sequence with no queries, decode token
+        W.custom([([], [3, 4]), ([(0, 40)], []), ([(0, 100), (200, 5)], [204])], H_q=8, H_kv=2, d=128, seed=2),
+        # MHA (H_q == H_kv) and d = 64
+        W.custom([([(0, 130), (140, 50)], list(range(140, 190)))], H_q=4, H_kv=4, d=64, seed=3),
+        # non-causal
+        W.custom([([(0, 70), (100, 30)], [10, 50, 120])], H_q=8, H_kv=2, d=128, seed=4, causal=0),
+        # peaky scores (q x 8) stress max subtraction and rescaling
+        W.custom([([(0, 400), (500, 100)], list(range(500, 600)))], H_q=8, H_kv=2, d=128, seed=6, qscale=4.0),
+        # decode with several query tokens per sequence and GQA 8
+        W.custom([([(0, 1000)], [997, 998, 999])], H_q=16, H_kv=2, d=128, seed=7),
+        # explicit scale
+        W.custom([([(0, 77)], list(range(60, 77)))], H_q=4, H_kv=1, d=128, seed=8, scale=0.05),
+    ]
+    for wl in cases:
+        _check(wl)
+        _check(wl, split_blocks=2)
+
+
+def test_empty_batch_and_no_queries():
+    wl = W.custom([([(0, 40)], [])], H_q=4, H_kv=1, d=128)
+    case = GpuCase(wl)
+    try:
+        msa.forward(case.q, case.desc, case.bt, case.pool, case.out, case.lse)
+        torch.cuda.synchronize()
+    finally:
+        case.close()
+
+
+def test_deterministic():
+    wl = W.random_case(60, batch=3, H_q=32, H_kv=8, d=128, max_ctx=900)
+    case = GpuCase(wl)
+    try:
+        ref = case.run(split_blocks=5)
+        for _ in range(4):
+            o, l = case.run(split_blocks=5)
+            assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o,
+                               ref[0].view(torch.int16) if o.dtype == torch.bfloat16 else ref[0])
+            assert torch.equal(l, ref[1]) or torch.equal(torch.isnan(l), torch.isnan(ref[1]))
+    finally:
+        case.close()
+
+
+def test_library_allocated_pool():
+    wl = W.random_case(61, batch=2, H_q=8, H_kv=2, d=128)
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16)
+    try:
+        kp, vp = pool.kv_ptrs()
+        K, V = wl.dense_pool("cuda")
+        torch.cuda.synchronize()
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        n = K.numel() * K.element_size()
+        assert hip.hipMemcpy(kp, K.data_ptr(), n, 3) == 0 and hip.hipMemcpy(vp, V.data_ptr(), n, 3) == 0
+        q = wl.q.cuda()
+        out = torch.empty_like(q)
+        lse = torch.empty(wl.total_q, wl.num_q_heads, device="cuda")
+        bt = torch.from_numpy(wl.block_table).cuda()
+        msa.forward(q, msa.SegDesc.from_workload(wl), bt, pool, out, lse)
+        torch.cuda.synchronize()
+    finally:
+        pool.close()
+    ref_out, ref_lse = oracle_result(wl)
+    compare(wl, out.cpu(), lse.cpu(), ref_out, ref_lse)
+
+
+# ---- benchmark configurations at full size (sampled rows) -----------------
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_benchmark_config_full_size(cfg):
+    wl = W.CONFIGS[cfg]()
+    rows = None if cfg == 3 else sample_rows(wl, 48, seed=cfg)
+    mx, mean = _check(wl, rows=rows)
+    print(f"[parity] config {cfg}: max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
