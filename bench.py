@@ -1,0 +1,218 @@
+"""Benchmark Multi-Segment Attention (libmsa) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline] [--no-secondary]
+
+One step is one msa_forward call over the whole workload: host planning, the
+plan upload and every kernel (chunk/prefill, decode, merge), with q, the K/V
+pool and the block table already resident in HBM.  The default workload is
+chunked prefill (4 sequences, GQA 32/8, head_dim 128, 4096-token context in 6
+scattered segments plus a 512-token chunk), reported in TFLOP/s of visible
+(query, key) pairs; the decode workload (64 sequences, 1k-8k-token contexts in
+2-16 segments over a 2M-token pool) is reported alongside in GB/s.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA attention TFLOP/s (prefill) and HBM GB/s (decode) vs MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = {"prefill": "kv_cache_attention_msa_amd/csrc/msa_prefill.hip",
+                  "decode": "kv_cache_attention_msa_amd/csrc/msa_decode.hip"}
+
+
+def visible_counts(wl):
+    """Per query row: number of keys it sees (k_pos <= q_pos when causal)."""
+    import numpy as np
+    counts = np.zeros(wl.total_q, dtype=np.int64)
+    seq_tokens = np.zeros(wl.batch, dtype=np.int64)
+    for b in range(wl.batch):
+        segs = wl.segs[wl.seg_offsets[b]:wl.seg_offsets[b + 1]]
+        starts, lens = segs[:, 0].astype(np.int64), segs[:, 1].astype(np.int64)
+        r = slice(wl.q_offsets[b], wl.q_offsets[b + 1])
+        qp = wl.q_pos[r].astype(np.int64)
+        if wl.causal:
+            c = np.clip(qp[:, None] - starts[None, :] + 1, 0, lens[None, :]).sum(axis=1)
+            seq_tokens[b] = int(np.clip(qp.max() - starts + 1, 0, lens).sum()) if len(qp) else 0
+        else:
+            c = np.full(len(qp), lens.sum())
+            seq_tokens[b] = lens.sum() if len(qp) else 0
+        counts[r] = c
+    return counts, seq_tokens
+
+
+def work_of(wl):
+    """Algorithmic FLOPs and HBM bytes of one MSA call."""
+    counts, seq_tokens = visible_counts(wl)
+    d, Hq, Hkv = wl.head_dim, wl.num_q_heads, wl.num_kv_heads
+    elt = 4 if wl.dtype == "fp32" else 2
+    flops = float(counts.sum()) * Hq * 4 * d
+    kv_bytes = float(seq_tokens.sum()) * Hkv * d * 2 * elt
+    io_bytes = wl.total_q * Hq * d * elt * 2 + wl.total_q * Hq * 4 + len(wl.block_table) * 4
+    return flops, kv_bytes + io_bytes
+
+
+def source_sha(rel):
+    p = os.path.join(ROOT, rel)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else None
+
+
+def traffic_for(kernel, units):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
+    kernel source still matches the one the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_src_sha") != source_sha(KERNEL_SOURCES[kernel]) or rec.get("units") != units:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_workload(wl, steps, warmup, kind):
+    import torch
+    import kv_cache_attention_msa_amd as msa
+
+    K, V = wl.dense_pool("cuda")
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K, v=V)
+    q = wl.q.cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(wl.total_q, wl.num_q_heads, dtype=torch.float32, device="cuda")
+    bt = torch.from_numpy(wl.block_table).cuda()
+    desc = msa.SegDesc.from_workload(wl)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        msa.forward(q, desc, bt, pool, out, lse, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        msa.forward(q, desc, bt, pool, out, lse, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # kernel-only timing: HIP events recorded by libmsa around each launch
+    pool.set_option(msa.OPT_TIMING, 1)
+    pool.kernel_time(kind, reset=True)
+    for _ in range(steps):
+        msa.forward(q, desc, bt, pool, out, lse, stream)
+    torch.cuda.synchronize()
+    times = {k: pool.kernel_time(k) for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE, msa.KERNEL_MERGE)}
+    # host planning + packing cost of one call (no device work): time the
+    # planner alone through its host-only export
+    t1 = time.perf_counter()
+    for _ in range(5):
+        msa.plan_debug(desc, wl.num_kv_heads, wl.head_dim, msa.BF16)
+    plan_ms = (time.perf_counter() - t1) / 5 * 1e3
+    pool.close()
+    del K, V
+    torch.cuda.empty_cache()
+    return wall / steps * 1e3, times, plan_ms
+
+
+def cpu_baseline(wl, flops_per_row, budget_s=12.0):
+    """The fp64 oracle on a bounded sample: whole sequences, taken in order,
+    until about budget_s of CPU time has been spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import attend
+    Kp, Vp = wl.sparse_pools_f64()
+    q64 = wl.q_f64()
+    done_rows, done_flops, t = 0, 0.0, 0.0
+    seqs = 0
+    for b in range(wl.batch):
+        r0, r1 = int(wl.q_offsets[b]), int(wl.q_offsets[b + 1])
+        t0 = time.perf_counter()
+        attend(q64, wl.q_offsets, wl.q_pos, wl.seg_offsets, wl.segs, wl.block_table, Kp, Vp,
+               wl.num_kv_heads, scale=wl.scale, causal=bool(wl.causal), rows=np.arange(r0, r1))
+        t += time.perf_counter() - t0
+        done_rows += r1 - r0
+        done_flops += float(flops_per_row[r0:r1].sum())
+        seqs += 1
+        if t >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": done_flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} of {wl.batch} sequences ({done_rows} query rows x {wl.num_q_heads} heads, "
+                      f"all their visible keys), fp64 numpy, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: MSA runs on a single MI355X here (no multi-GPU path).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import kv_cache_attention_msa_amd as msa
+    import workloads as W
+
+    msa.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.CONFIGS[args.config]()
+    flops, nbytes = work_of(wl)
+    counts, _ = visible_counts(wl)
+    ms, times, plan_ms = run_workload(wl, args.steps, args.warmup, msa.KERNEL_PREFILL)
+    pre_ms, pre_n = times[msa.KERNEL_PREFILL]
+    dec_ms, dec_n = times[msa.KERNEL_DECODE]
+    mrg_ms, mrg_n = times[msa.KERNEL_MERGE]
+    value = flops / (ms * 1e-3) / 1e12
+    # dominant kernel: the chunk (prefill) kernel; one launch processes the whole workload
+    k_avg = pre_ms / max(pre_n, 1)
+    achieved = flops / (k_avg * 1e-3) / 1e12 if pre_n else None
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
+                "traffic": traffic_for("prefill", wl.name),
+                "kernel": "msa_prefill (bf16 MFMA)", "kernel_ms": k_avg,
+                "merge_ms": mrg_ms / mrg_n if mrg_n else 0.0, "launches_per_step": (pre_n + dec_n + mrg_n) / args.steps}
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": 16, "total_q": wl.total_q,
+                   "segments": int(len(wl.segs)), "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                   "host_plan_ms": plan_ms},
+        "roofline": roofline,
+    }
+    if not args.no_secondary:
+        wl3 = W.config3()
+        f3, b3 = work_of(wl3)
+        ms3, t3, plan3 = run_workload(wl3, args.steps, args.warmup, msa.KERNEL_DECODE)
+        d_ms, d_n = t3[msa.KERNEL_DECODE]
+        m_ms, m_n = t3[msa.KERNEL_MERGE]
+        d_avg = d_ms / max(d_n, 1)
+        ach = b3 / (d_avg * 1e-3) / 1e9 if d_n else None
+        line["secondary"] = {
+            "workload": wl3.name, "metric": "decode HBM GB/s", "value": b3 / (ms3 * 1e-3) / 1e9, "unit": "GB/s",
+            "ms_per_step": ms3, "algorithmic_bytes": b3, "algorithmic_flops": f3, "host_plan_ms": plan3,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": ach / PEAK_HBM_GBS if ach else None,
+                         "traffic": traffic_for("decode", wl3.name), "kernel": "msa_decode",
+                         "kernel_ms": d_avg, "merge_ms": m_ms / m_n if m_n else 0.0},
+        }
+        del wl3
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, counts * wl.num_q_heads * 4 * wl.head_dim)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,8 +53,8 @@ extern "C" {
 /* A block-paged KV pool: two device arrays K and V, each laid out
  * [num_blocks][num_kv_heads][MSA_BLOCK_SIZE][head_dim], row-major, of `dtype`.
  * One (block, kv head) tile is contiguous (4 KiB for bf16 and head_dim 128).
- * The pool also owns the library's per-call workspace (plan upload area,
- * partial results of split work) and pinned host staging. */
+ * The pool also owns the library's per-call workspace (device plan buffer,
+ * partial results of split work) and pinned, device-mapped host staging. */
 typedef struct msa_pool msa_pool;
 
 typedef struct {
@@ -111,7 +111,7 @@ typedef struct {
   const int32_t* seg_offsets;  /* [batch+1], seg_offsets[0] == 0, non-decreasing     */
   const msa_segment* segs;     /* [seg_offsets[batch]]                               */
   int32_t block_table_len;     /* entries in block_table                            */
-  float scale;                 /* score scale; 0 selects 1/sqrt(head_dim)            */
+  float scale;                 /* score scale, >= 0; 0 selects 1/sqrt(head_dim)      */
   int32_t causal;              /* 1: key visible iff k_pos <= q_pos; 0: all visible   */
 } msa_seg_desc;
 
@@ -151,6 +151,7 @@ int msa_pool_set_option(msa_pool* pool, int32_t option, int64_t value);
 #define MSA_KERNEL_DECODE  1    /* bf16 bandwidth-bound decode kernel               */
 #define MSA_KERNEL_FP32    2    /* fp32 kernel                                      */
 #define MSA_KERNEL_MERGE   3    /* log-sum-exp merge of split partials              */
+#define MSA_KERNEL_UPLOAD  4    /* copy of the per-call plan into device memory     */
 
 /* With MSA_OPT_TIMING on: total device time (ms, from HIP events recorded on
  * the launch stream around each launch) and number of launches of `kind`

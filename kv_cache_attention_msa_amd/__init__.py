@@ -17,7 +17,7 @@ import numpy as np
 __all__ = [
     "MsaError", "Pool", "SegDesc", "forward", "plan_debug", "library_path", "load_library",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
-    "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE",
+    "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD",
     "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS",
 ]
 
@@ -26,7 +26,7 @@ SEG_FRESH = 1
 BLOCK_SIZE = 16
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS = 1, 2, 3
-KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE = 0, 1, 2, 3
+KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_last_error",

@@ -4,10 +4,12 @@
 //   1. checks every argument and builds the plan on the host (no HIP call
 //      before this succeeds, so an error leaves the stream untouched);
 //   2. packs the plan (block list, query positions, work and merge items) into
-//      one of two pinned staging buffers and enqueues a single host-to-device
-//      copy into the pool's workspace on the caller's stream;
-//   3. enqueues the prefill, decode and fp32 kernels for the items of each
-//      kind, then the merge kernel when some tile was split over KV.
+//      the next pinned, device-mapped staging buffer of a small ring;
+//   3. enqueues on the caller's stream: a copy kernel that moves the plan into
+//      the pool's device plan buffer, the prefill, decode and fp32 kernels for
+//      the items of each kind, then the merge kernel when some tile was split
+//      over KV.  Everything is on the caller's stream, so consecutive calls
+//      are ordered without cross-stream events.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -15,7 +17,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 
 #include "msa_internal.h"
 
@@ -79,23 +80,31 @@ struct msa_pool {
   int32_t split_blocks = 0;
   int32_t num_cus_override = 0;
 
-  // device workspace: [plan upload area | partial O | partial lse]
-  void* d_ws = nullptr;
-  size_t ws_bytes = 0;
-  // pinned staging, two buffers used alternately
-  void* h_stage[2] = {nullptr, nullptr};
-  size_t stage_bytes[2] = {0, 0};
-  hipEvent_t stage_done[2] = {nullptr, nullptr};
-  bool stage_pending[2] = {false, false};
-  int stage_next = 0;
+  // Plan upload: call n packs its plan into pinned, device-mapped staging
+  // buffer n % kSlots; a small kernel on the caller's stream copies it into the
+  // device plan buffer ahead of the attention kernels (same queue, so no
+  // cross-engine hand-off).  A staging buffer is rewritten only once the copy
+  // that read it has run (event), which in steady state is long done.
+  static constexpr int kSlots = 3;
+  void* h_stage[kSlots] = {};
+  void* h_stage_dev[kSlots] = {};      // device address of the same pinned memory
+  size_t stage_bytes[kSlots] = {};
+  hipEvent_t stage_done[kSlots] = {};
+  bool stage_pending[kSlots] = {};
+  int next_slot = 0;
+  void* d_plan = nullptr;
+  size_t plan_cap = 0;
+  // partial results of KV-split tiles
+  void* d_part = nullptr;
+  size_t part_bytes = 0;
   hipStream_t last_stream = nullptr;
   bool used = false;
 
   // timing
   std::vector<TimingRecord> records;
   std::vector<hipEvent_t> spare_events;
-  double total_ms[kNumKinds] = {0, 0, 0, 0};
-  int64_t launches[kNumKinds] = {0, 0, 0, 0};
+  double total_ms[kNumKinds] = {};
+  int64_t launches[kNumKinds] = {};
 
   Plan plan;
 };
@@ -147,32 +156,38 @@ int timed_launch(msa_pool* p, int kind, hipStream_t stream, F&& launch) {
   return MSA_OK;
 }
 
-int ensure_device_ws(msa_pool* p, size_t bytes, hipStream_t stream) {
-  if (bytes <= p->ws_bytes) return MSA_OK;
-  size_t want = std::max(bytes, p->ws_bytes + p->ws_bytes / 2);
-  want = align_up(want, size_t(1) << 20);
-  if (p->d_ws) {
-    // Work already enqueued may still read the old workspace.
+int grow_device(void** ptr, size_t* cap, size_t bytes, const char* what) {
+  if (bytes <= *cap) return MSA_OK;
+  const size_t want = align_up(std::max(bytes, *cap + *cap / 2), size_t(1) << 16);
+  if (*ptr) {
+    MSA_HIP(hipFree(*ptr));
+    *ptr = nullptr;
+    *cap = 0;
+  }
+  hipError_t e = hipMalloc(ptr, want);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    (void)hipGetLastError();
+    return set_error(MSA_ERR_OOM, "%s hipMalloc(%zu) failed: %s", what, want, hipGetErrorString(e));
+  }
+  *cap = want;
+  return MSA_OK;
+}
+
+// Device buffers read by kernels of earlier calls are only replaced once the
+// streams that used them have drained.
+int ensure_device(msa_pool* p, void** ptr, size_t* cap, size_t bytes, hipStream_t stream, const char* what) {
+  if (bytes <= *cap) return MSA_OK;
+  if (*ptr) {
     if (p->used) MSA_HIP(hipStreamSynchronize(p->last_stream));
     MSA_HIP(hipStreamSynchronize(stream));
-    MSA_HIP(hipFree(p->d_ws));
-    p->d_ws = nullptr;
-    p->ws_bytes = 0;
   }
-  hipError_t e = hipMalloc(&p->d_ws, want);
-  if (e != hipSuccess) {
-    p->d_ws = nullptr;
-    (void)hipGetLastError();
-    return set_error(MSA_ERR_OOM, "workspace hipMalloc(%zu) failed: %s", want, hipGetErrorString(e));
-  }
-  p->ws_bytes = want;
-  return MSA_OK;
+  return grow_device(ptr, cap, bytes, what);
 }
 
 int ensure_stage(msa_pool* p, int slot, size_t bytes) {
   if (!p->stage_done[slot]) MSA_HIP(hipEventCreateWithFlags(&p->stage_done[slot], hipEventDisableTiming));
   if (p->stage_pending[slot]) {
-    // The copy that last read this buffer must have finished before we rewrite it.
     MSA_HIP(hipEventSynchronize(p->stage_done[slot]));
     p->stage_pending[slot] = false;
   }
@@ -180,15 +195,16 @@ int ensure_stage(msa_pool* p, int slot, size_t bytes) {
   size_t want = align_up(std::max(bytes, p->stage_bytes[slot] * 3 / 2), size_t(1) << 16);
   if (p->h_stage[slot]) {
     MSA_HIP(hipHostFree(p->h_stage[slot]));
-    p->h_stage[slot] = nullptr;
+    p->h_stage[slot] = p->h_stage_dev[slot] = nullptr;
     p->stage_bytes[slot] = 0;
   }
-  hipError_t e = hipHostMalloc(&p->h_stage[slot], want, hipHostMallocDefault);
+  hipError_t e = hipHostMalloc(&p->h_stage[slot], want, hipHostMallocMapped);
   if (e != hipSuccess) {
     p->h_stage[slot] = nullptr;
     (void)hipGetLastError();
     return set_error(MSA_ERR_OOM, "pinned hipHostMalloc(%zu) failed: %s", want, hipGetErrorString(e));
   }
+  MSA_HIP(hipHostGetDevicePointer(&p->h_stage_dev[slot], p->h_stage[slot], 0));
   p->stage_bytes[slot] = want;
   return MSA_OK;
 }
@@ -251,7 +267,7 @@ int msa_pool_kv_ptrs(const msa_pool* pool, void** k, void** v) {
 int msa_destroy_pool(msa_pool* p) {
   if (!p) return MSA_OK;
   int rc = MSA_OK;
-  const bool touched = p->used || p->owns_kv || p->d_ws || p->h_stage[0] || p->h_stage[1];
+  const bool touched = p->used || p->owns_kv || p->d_plan || p->d_part || p->h_stage[0];
   if (touched) {
     DeviceGuard g(p->desc.device);
     if (p->used && hipStreamSynchronize(p->last_stream) != hipSuccess) rc = MSA_ERR_HIP;
@@ -260,11 +276,12 @@ int msa_destroy_pool(msa_pool* p) {
       (void)hipEventDestroy(r.stop);
     }
     for (auto e : p->spare_events) (void)hipEventDestroy(e);
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < msa_pool::kSlots; ++s) {
       if (p->stage_done[s]) (void)hipEventDestroy(p->stage_done[s]);
       if (p->h_stage[s]) (void)hipHostFree(p->h_stage[s]);
     }
-    if (p->d_ws) (void)hipFree(p->d_ws);
+    if (p->d_plan) (void)hipFree(p->d_plan);
+    if (p->d_part) (void)hipFree(p->d_part);
     if (p->owns_kv) {
       (void)hipFree(p->k);
       (void)hipFree(p->v);
@@ -394,14 +411,17 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   const size_t off_merge = off;
   off = align_up(off + plan.merges.size() * sizeof(MergeItem), 256);
   const size_t plan_bytes = off;
-  const size_t off_part_o = plan_bytes;
-  const size_t off_part_lse = align_up(off_part_o + (size_t)plan.part_rows * D * sizeof(float), 256);
-  const size_t ws_need = align_up(off_part_lse + (size_t)plan.part_rows * sizeof(float), 256);
+  const size_t off_part_lse = align_up((size_t)plan.part_rows * D * sizeof(float), 256);
+  const size_t part_need = off_part_lse + align_up((size_t)plan.part_rows * sizeof(float), 256);
 
-  rc = ensure_device_ws(p, ws_need, stream);
+  if (part_need > 0) {
+    rc = ensure_device(p, &p->d_part, &p->part_bytes, part_need, stream, "partial-result buffer");
+    if (rc) return rc;
+  }
+  rc = ensure_device(p, &p->d_plan, &p->plan_cap, plan_bytes, stream, "plan buffer");
   if (rc) return rc;
-  const int slot = p->stage_next;
-  p->stage_next ^= 1;
+  const int slot = p->next_slot;
+  p->next_slot = (p->next_slot + 1) % msa_pool::kSlots;
   rc = ensure_stage(p, slot, plan_bytes);
   if (rc) return rc;
   char* h = (char*)p->h_stage[slot];
@@ -412,8 +432,9 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
       memcpy(h + off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
   if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
 
-  char* dws = (char*)p->d_ws;
-  MSA_HIP(hipMemcpyAsync(dws, h, plan_bytes, hipMemcpyHostToDevice, stream));
+  char* dws = (char*)p->d_plan;
+  rc = timed_launch(p, kUpload, stream, [&]() { return launch_upload(p->h_stage_dev[slot], dws, plan_bytes, stream); });
+  if (rc) return rc;
   MSA_HIP(hipEventRecord(p->stage_done[slot], stream));
   p->stage_pending[slot] = true;
   p->used = true;
@@ -431,8 +452,8 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   a.q_pos = (const int32_t*)(dws + off_qpos);
   a.merges = (const MergeItem*)(dws + off_merge);
   a.n_merges = (int32_t)plan.merges.size();
-  a.part_o = (float*)(dws + off_part_o);
-  a.part_lse = (float*)(dws + off_part_lse);
+  a.part_o = (float*)p->d_part;
+  a.part_lse = (float*)((char*)p->d_part + off_part_lse);
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = p->desc.num_kv_heads;
   a.group = desc->num_q_heads / p->desc.num_kv_heads;
@@ -444,6 +465,7 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
     if (plan.items[k].empty()) continue;
     a.items = (const WorkItem*)(dws + off_items[k]);
     a.n_items = (int32_t)plan.items[k].size();
+    a.max_mrows = plan.max_mrows[k];
     rc = timed_launch(p, k, stream, [&]() {
       if (k == kPrefill) return launch_prefill(a, D, stream);
       if (k == kDecode) return launch_decode(a, D, stream);

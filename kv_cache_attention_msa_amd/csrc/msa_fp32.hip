@@ -1,4 +1,4 @@
-// Row-at-a-time MSA kernel (fp32 pools; element type templated).
+// Row-at-a-time MSA kernel for fp32 pools.
 //
 // One wave owns one (query row, q head) pair at a time and walks the work
 // item's KV blocks in position order: lanes split head_dim, each key's score
@@ -84,12 +84,6 @@ static int launch_rowwise(const KernelArgs& a, int head_dim, void* stream) {
 
 int launch_fp32(const KernelArgs& a, int head_dim, void* stream) {
   return launch_rowwise<float>(a, head_dim, stream);
-}
-
-// Row-at-a-time path for bf16 pools; used by the bf16 launchers while their
-// dedicated kernels are not selected.
-int launch_rowwise_bf16(const KernelArgs& a, int head_dim, void* stream) {
-  return launch_rowwise<bf16_t>(a, head_dim, stream);
 }
 
 }  // namespace msa

@@ -12,7 +12,7 @@ namespace msa {
 
 constexpr int kBlock = MSA_BLOCK_SIZE;
 constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per prefill tile
-constexpr int kDecodeMRows = 16;     // pairs per decode tile (one MFMA column block)
+constexpr int kDecodeMRows = 8;      // pairs per decode tile (at most 8 of the 16 MFMA columns)
 constexpr int kFp32MRows = 64;       // pairs per fp32 tile
 constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accepted
 constexpr int kBtIndexBits = 28;     // block-table index bits in BlockEntry::bt_valid
@@ -33,7 +33,7 @@ struct WorkItem {
   int32_t blk_end;
   int32_t part_row;  // -1: final output; else first row of this split's partials
   int32_t seq;
-  int32_t pad;
+  int32_t q_min;     // smallest query position of the tile (causal fast path)
 };
 
 // Rows of one tile that was split over KV: n_splits partials of n_mrows rows
@@ -49,7 +49,8 @@ struct MergeItem {
 };
 
 enum Kind { kPrefill = MSA_KERNEL_PREFILL, kDecode = MSA_KERNEL_DECODE,
-            kFp32 = MSA_KERNEL_FP32, kMerge = MSA_KERNEL_MERGE, kNumKinds = 4 };
+            kFp32 = MSA_KERNEL_FP32, kMerge = MSA_KERNEL_MERGE, kUpload = MSA_KERNEL_UPLOAD,
+            kNumKinds = 5 };
 
 struct Plan {
   std::vector<BlockEntry> blocks;
@@ -57,6 +58,7 @@ struct Plan {
   std::vector<WorkItem> items[3];   // per kernel kind (prefill, decode, fp32)
   std::vector<MergeItem> merges;
   int64_t part_rows = 0;            // partial rows (each head_dim floats + 1 lse)
+  int32_t max_mrows[3] = {0, 0, 0}; // largest (query row, head) count of an item, per kind
   int32_t total_q = 0;
 };
 
@@ -93,6 +95,7 @@ struct KernelArgs {
   int32_t group;          // num_q_heads / num_kv_heads
   int32_t causal;
   float scale_log2;       // scale * log2(e)
+  int32_t max_mrows;      // largest n_q * group among the launch's items
 };
 
 // Launchers (msa_kernels.hip).  Return a hipError_t value.
@@ -100,5 +103,7 @@ int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
 int launch_decode(const KernelArgs& a, int head_dim, void* stream);
 int launch_fp32(const KernelArgs& a, int head_dim, void* stream);
 int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream);
+// Copies `bytes` (a multiple of 16) from device-mapped pinned host memory.
+int launch_upload(const void* src, void* dst, size_t bytes, void* stream);
 
 }  // namespace msa

@@ -35,7 +35,7 @@ static int fail(std::string& err, int code, const char* fmt, ...) {
 namespace {
 
 struct Tile {
-  int32_t kind, seq, kv_head, q_row0, n_q, blk_begin, blk_end;
+  int32_t kind, seq, q_min, q_row0, n_q, blk_begin, blk_end;
 };
 
 // Largest block-count of one work item before the planner splits a tile.
@@ -57,6 +57,7 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   plan.merges.clear();
   plan.part_rows = 0;
   plan.total_q = 0;
+  for (auto& x : plan.max_mrows) x = 0;
 
   if (!d) return fail(err, INV, "seg_desc is NULL");
   if (cfg.head_dim != 64 && cfg.head_dim != 128)
@@ -72,7 +73,8 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   const int group = d->num_q_heads / cfg.num_kv_heads;
   if (group > kMaxGroup) return fail(err, UNS, "GQA ratio %d exceeds %d", group, kMaxGroup);
   if (d->causal != 0 && d->causal != 1) return fail(err, INV, "causal must be 0 or 1");
-  if (!std::isfinite(d->scale)) return fail(err, INV, "scale is not finite");
+  if (!std::isfinite(d->scale) || d->scale < 0.f)
+    return fail(err, INV, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
   if (d->block_table_len < 0) return fail(err, INV, "block_table_len < 0");
   if (d->block_table_len > (1 << kBtIndexBits))
     return fail(err, MSA_ERR_WORKSPACE, "block_table_len %d exceeds 2^%d", d->block_table_len,
@@ -155,15 +157,18 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
     for (int32_t r = q0; r < q1; r += tile_rows) {
       const int32_t n = std::min(tile_rows, q1 - r);
       int32_t end = seq_blk1;
+      int32_t qmin = d->q_pos[r], qmax = d->q_pos[r];
+      for (int32_t i = r + 1; i < r + n; ++i) {
+        qmin = std::min(qmin, d->q_pos[i]);
+        qmax = std::max(qmax, d->q_pos[i]);
+      }
       if (d->causal) {
-        int32_t qmax = d->q_pos[r];
-        for (int32_t i = r + 1; i < r + n; ++i) qmax = std::max(qmax, d->q_pos[i]);
         // first block whose slot-0 position is beyond every query of the tile
         auto it = std::upper_bound(plan.blocks.begin() + seq_blk0, plan.blocks.begin() + seq_blk1,
                                    qmax, [](int32_t v, const BlockEntry& e) { return v < e.pos0; });
         end = (int32_t)(it - plan.blocks.begin());
       }
-      tiles.push_back(Tile{kind, b, 0, r, n, seq_blk0, end});
+      tiles.push_back(Tile{kind, b, qmin, r, n, seq_blk0, end});
     }
   }
   plan.q_pos.assign(d->q_pos, d->q_pos + total_q);
@@ -185,9 +190,10 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
     nsplit = std::min(nsplit, (nblk + align - 1) / align);
     if (nsplit < 1) nsplit = 1;
     const int32_t n_mrows = t.n_q * group;
+    plan.max_mrows[t.kind] = std::max(plan.max_mrows[t.kind], n_mrows);
     for (int32_t h = 0; h < cfg.num_kv_heads; ++h) {
       if (nsplit == 1) {
-        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, 0});
+        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, t.q_min});
         continue;
       }
       if ((int64_t)plan.part_rows + (int64_t)nsplit * n_mrows > std::numeric_limits<int32_t>::max())
@@ -199,7 +205,7 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
         const int32_t u1 = (int32_t)((int64_t)units * (s + 1) / nsplit);
         const int32_t b1 = std::min(nblk, u1 * align);
         plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin + done,
-                                              t.blk_begin + b1, part0 + s * n_mrows, t.seq, 0});
+                                              t.blk_begin + b1, part0 + s * n_mrows, t.seq, t.q_min});
         done = b1;
       }
       plan.merges.push_back(MergeItem{h, t.q_row0, t.n_q, part0, nsplit, n_mrows, 0, 0});
