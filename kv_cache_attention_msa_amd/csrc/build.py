@@ -28,6 +28,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{HERE}", "-Wall", "-
 # Packed fp32 ops stay off: the kernels are written for scalar fp32 VALU math.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
+# The bf16 attention kernels never feed NaN into their max/exp arithmetic (pool
+# slots outside the segments are selected out or zeroed), so max needs no
+# NaN canonicalisation there.
+NO_NAN_SOURCES = {"msa_prefill.hip", "msa_decode.hip"}
 
 
 def hipcc() -> str:
@@ -51,6 +55,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in HOST_SOURCES + HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         extra = DEVICE + ["-x", "hip"] if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"]
+        if src in NO_NAN_SOURCES:
+            extra = ["-fno-honor-nans"] + extra
         cmds.append([cc, "-c"] + COMMON + extra + [os.path.join(HERE, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:

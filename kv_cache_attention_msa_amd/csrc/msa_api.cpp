@@ -222,6 +222,8 @@ int msa_create_pool(const msa_pool_desc* desc, void* k_base, void* v_base, msa_p
   *out = nullptr;
   if (desc->num_blocks <= 0 || desc->num_kv_heads <= 0)
     return set_error(MSA_ERR_INVALID_ARG, "num_blocks and num_kv_heads must be > 0");
+  if (desc->num_blocks > kMaxPoolBlocks)
+    return set_error(MSA_ERR_UNSUPPORTED, "num_blocks %d exceeds %d", desc->num_blocks, kMaxPoolBlocks);
   if (desc->block_size != MSA_BLOCK_SIZE)
     return set_error(MSA_ERR_UNSUPPORTED, "block_size %d is not supported (16)", desc->block_size);
   if (desc->head_dim != 64 && desc->head_dim != 128)
@@ -399,8 +401,11 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   // ---- pack the plan ----
   const int D = p->desc.head_dim;
   size_t off = 0;
+  // The block list is followed by kBlockPad zero entries so that a kernel may
+  // always read the entries of a step (their valid counts are ignored).
+  constexpr size_t kBlockPad = 4;
   const size_t off_blocks = off;
-  off = align_up(off + plan.blocks.size() * sizeof(BlockEntry), 256);
+  off = align_up(off + (plan.blocks.size() + kBlockPad) * sizeof(BlockEntry), 256);
   const size_t off_qpos = off;
   off = align_up(off + plan.q_pos.size() * sizeof(int32_t), 256);
   size_t off_items[3];
@@ -426,6 +431,7 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   if (rc) return rc;
   char* h = (char*)p->h_stage[slot];
   if (!plan.blocks.empty()) memcpy(h + off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
+  memset(h + off_blocks + plan.blocks.size() * sizeof(BlockEntry), 0, kBlockPad * sizeof(BlockEntry));
   memcpy(h + off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
   for (int k = 0; k < 3; ++k)
     if (!plan.items[k].empty())
@@ -433,7 +439,10 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
 
   char* dws = (char*)p->d_plan;
-  rc = timed_launch(p, kUpload, stream, [&]() { return launch_upload(p->h_stage_dev[slot], dws, plan_bytes, stream); });
+  rc = timed_launch(p, kUpload, stream, [&]() {
+    return launch_upload(p->h_stage_dev[slot], dws, plan_bytes, (int32_t)plan.blocks.size(), block_table,
+                         p->desc.num_blocks, stream);
+  });
   if (rc) return rc;
   MSA_HIP(hipEventRecord(p->stage_done[slot], stream));
   p->stage_pending[slot] = true;

@@ -28,7 +28,8 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
 
-__device__ __forceinline__ int entry_bt(const BlockEntry& e) {
+// Pool block id of a device-side block entry (resolved by the upload kernel).
+__device__ __forceinline__ int entry_block(const BlockEntry& e) {
   return (int)((uint32_t)e.bt_valid & ((1u << kBtIndexBits) - 1u));
 }
 __device__ __forceinline__ int entry_valid(const BlockEntry& e) {

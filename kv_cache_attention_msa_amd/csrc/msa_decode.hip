@@ -43,7 +43,7 @@ struct BlockMeta {
 
 __device__ __forceinline__ BlockMeta block_meta(const KernelArgs& a, int idx) {
   const BlockEntry e = a.blocks[idx];
-  return BlockMeta{a.block_table[entry_bt(e)], e.pos0, entry_valid(e)};
+  return BlockMeta{entry_block(e), e.pos0, entry_valid(e)};
 }
 
 template <int D>

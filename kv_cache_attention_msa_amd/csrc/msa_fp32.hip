@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void msa_rowwise_kernel(KernelArgs a) {
     for (int b = it.blk_begin; b < it.blk_end; ++b) {
       const BlockEntry be = a.blocks[b];
       const int valid = entry_valid(be);
-      const int64_t phys = a.block_table[entry_bt(be)];
+      const int64_t phys = entry_block(be);
       const int64_t base = (phys * a.num_kv_heads + it.kv_head) * (int64_t)(kBlock * D);
       for (int s = 0; s < valid; ++s) {
         if (a.causal && be.pos0 + s > qp) break;

@@ -15,11 +15,15 @@ constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per pre
 constexpr int kDecodeMRows = 8;      // pairs per decode tile (at most 8 of the 16 MFMA columns)
 constexpr int kFp32MRows = 64;       // pairs per fp32 tile
 constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accepted
-constexpr int kBtIndexBits = 28;     // block-table index bits in BlockEntry::bt_valid
+constexpr int kBtIndexBits = 28;     // index bits in BlockEntry::bt_valid
+constexpr int kMaxPoolBlocks = 1 << kBtIndexBits;
 
-// One entry of a sequence's position-ordered block list (8 bytes on device).
+// One entry of a sequence's position-ordered block list (8 bytes).  The host
+// writes the block-table index; the upload kernel replaces it, on the device,
+// by the pool block id it names, so kernels never chase block_table.
 struct BlockEntry {
-  int32_t bt_valid;  // bits 0..27: index into block_table; bits 28..31: valid slots - 1
+  int32_t bt_valid;  // bits 0..27: block-table index (host) / pool block id (device);
+                     // bits 28..31: valid slots - 1
   int32_t pos0;      // absolute position of slot 0
 };
 
@@ -103,7 +107,10 @@ int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
 int launch_decode(const KernelArgs& a, int head_dim, void* stream);
 int launch_fp32(const KernelArgs& a, int head_dim, void* stream);
 int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream);
-// Copies `bytes` (a multiple of 16) from device-mapped pinned host memory.
-int launch_upload(const void* src, void* dst, size_t bytes, void* stream);
+// Copies `bytes` (a multiple of 16) of plan from device-mapped pinned host
+// memory to `dst`, resolving the first `n_blocks` entries (the block list)
+// through `block_table`; ids outside [0, num_blocks) are clamped into range.
+int launch_upload(const void* src, void* dst, size_t bytes, int32_t n_blocks, const int32_t* block_table,
+                  int32_t num_blocks, void* stream);
 
 }  // namespace msa

@@ -2,9 +2,9 @@
 // 128 (query row, q head) pairs against a run of KV blocks, with both matrix
 // products on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 //
-// Work-group: 4 waves; wave w owns tile rows 32w..32w+31.  A tile row is a
-// (query row, head of the kv head's GQA group) pair, so the K/V tile staged in
-// LDS serves every q head of the group.
+// Work-group: 4 waves; wave w owns tile rows 32w..32w+31; two work-groups
+// share a CU.  A tile row is a (query row, head of the kv head's GQA group)
+// pair, so the K/V tile staged in LDS serves every q head of the group.
 //
 // Per step of 64 keys (4 pool blocks of the position-ordered block list, which
 // may span segment boundaries):
@@ -36,23 +36,28 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
 
+// LDS tiles are kept as two arrays of 8-byte halves: every 16-byte MFMA
+// operand is read with two ds_read_b64 (on gfx950 64-bit LDS reads sustain
+// about twice the bytes per clock of 128-bit reads).  Half h of 16-byte chunk
+// c of a row lives in array h at the row's swizzled chunk position.
 template <int D>
 struct PrefillSmem {
-  uint4 k[2][kStepKeys * D / 8];   // [key][D], 16-byte chunks swizzled
-  uint4 vt[2][D * kStepKeys / 8];  // [d][64 keys], keys permuted, chunks swizzled
+  uint2 k[2][2][kStepKeys][D / 8];   // [buf][half][key][chunk]: K rows (head_dim)
+  uint2 vt[2][2][D][kStepKeys / 8];  // [buf][half][d][chunk]: V transposed (64 keys)
 };
 
-// XOR swizzle of 16-byte chunks for rows of 8 chunks (128 bytes): any 8
-// consecutive rows, and any 16 consecutive rows of one parity, map a chunk
-// index to distinct chunk positions.
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
-
+// Chunk swizzles.  With 8-byte halves a row of the K array is 16 (D=128) or
+// 8 (D=64) bank pairs wide and a row of the Vt array 8 bank pairs wide; the
+// 16 lanes that LDS serves together read 16 consecutive rows at one chunk
+// index and must land on 16 distinct bank pairs.
 template <int D>
-__device__ __forceinline__ int k_chunk(int row, int c) {
-  if constexpr (D == 128) return row * 16 + (c ^ (row & 15));
-  else return row * 8 + (c ^ swz8(row));
+__device__ __forceinline__ int k_swz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
 }
-__device__ __forceinline__ int vt_chunk(int d, int c) { return d * 8 + (c ^ swz8(d)); }
+// Vt rows: distinct positions for each parity class of 16 aligned rows
+// (operand reads), and for 8 rows spaced 8 apart (transposed writes).
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 7; }
 
 // Position of local key k (0..63) inside a transposed V row: bits 2 and 3 of
 // k are swapped so that the 8 keys one lane feeds to the PV MFMA are adjacent.
@@ -67,35 +72,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+// Operand loads.  The two 8-byte halves of one operand are 8 KiB (K, D=128)
+// or 4 KiB apart and merge into one ds_read2st64_b64 whose 4 result registers
+// are the operand in order.  The empty asm hides the relation between the
+// addresses of different operands, so that the compiler pairs the halves of
+// the same operand (and not the low halves of two operands, which then need
+// register moves).
+template <int D>
+__device__ __forceinline__ bf16x8 ld_k(const PrefillSmem<D>& sm, int buf, int row, int c) {
+  int off = (row * (D / 8) + (c ^ k_swz<D>(row))) * 8;
+  asm volatile("" : "+v"(off));
+  const char* base = (const char*)&sm.k[buf][0][0][0];
+  const uint2 lo = *(const uint2*)(base + off);
+  const uint2 hi = *(const uint2*)(base + off + kStepKeys * D);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 ld_vt(const PrefillSmem<D>& sm, int buf, int d, int c) {
+  int off = (d * (kStepKeys / 8) + (c ^ vt_swz(d))) * 8;
+  asm volatile("" : "+v"(off));
+  const char* base = (const char*)&sm.vt[buf][0][0][0];
+  const uint2 lo = *(const uint2*)(base + off);
+  const uint2 hi = *(const uint2*)(base + off + D * kStepKeys);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // Descriptors of one step's (up to) 4 blocks.  Plain scalar fields rather
 // than arrays, so that no private array is ever indexed at run time.
 struct StepMeta {
   int nb;                          // blocks in this step (1..4)
-  int ph0, ph1, ph2, ph3;          // pool block ids
+  int ph0, ph1, ph2, ph3;          // pool block ids (always valid ids)
   int ps0, ps1, ps2, ps3;          // positions of slot 0
   int vl0, vl1, vl2, vl3;          // valid slots (0 past the item's end)
+  bool full;                       // 64 keys, all visible to every row of the tile
   __device__ __forceinline__ int phys(int b) const { return b == 0 ? ph0 : b == 1 ? ph1 : b == 2 ? ph2 : ph3; }
   __device__ __forceinline__ int pos0(int b) const { return b == 0 ? ps0 : b == 1 ? ps1 : b == 2 ? ps2 : ps3; }
   __device__ __forceinline__ int valid(int b) const { return b == 0 ? vl0 : b == 1 ? vl1 : b == 2 ? vl2 : vl3; }
 };
 
-// Branch-free so that the step descriptors stay in (scalar) registers: blocks
-// past the item's end re-read its last entry and get valid = 0.
-__device__ __forceinline__ void load_meta(const KernelArgs& a, int blk, int blk_end, StepMeta& m) {
-  m.nb = min(4, blk_end - blk);
-  const BlockEntry e0 = a.blocks[blk];
-  const BlockEntry e1 = a.blocks[min(blk + 1, blk_end - 1)];
-  const BlockEntry e2 = a.blocks[min(blk + 2, blk_end - 1)];
-  const BlockEntry e3 = a.blocks[min(blk + 3, blk_end - 1)];
-  m.ph0 = a.block_table[entry_bt(e0)];
-  m.ph1 = a.block_table[entry_bt(e1)];
-  m.ph2 = a.block_table[entry_bt(e2)];
-  m.ph3 = a.block_table[entry_bt(e3)];
+// The block list is padded with 4 spare entries and indices are clamped to
+// them, so the entries of any step (also one past the item's last) are
+// readable; entries past the item's end get valid = 0 (their ids are still
+// pool block ids, so loads from them stay in bounds).
+__device__ __forceinline__ void load_meta(const KernelArgs& a, int blk, int blk_end, int q_min, StepMeta& m) {
+  m.nb = max(0, min(4, blk_end - blk));
+  const int last = blk_end + 3;
+  const BlockEntry e0 = a.blocks[min(blk, last)], e1 = a.blocks[min(blk + 1, last)];
+  const BlockEntry e2 = a.blocks[min(blk + 2, last)], e3 = a.blocks[min(blk + 3, last)];
+  m.ph0 = entry_block(e0); m.ph1 = entry_block(e1); m.ph2 = entry_block(e2); m.ph3 = entry_block(e3);
   m.ps0 = e0.pos0; m.ps1 = e1.pos0; m.ps2 = e2.pos0; m.ps3 = e3.pos0;
-  m.vl0 = entry_valid(e0);
+  m.vl0 = m.nb > 0 ? entry_valid(e0) : 0;
   m.vl1 = m.nb > 1 ? entry_valid(e1) : 0;
   m.vl2 = m.nb > 2 ? entry_valid(e2) : 0;
   m.vl3 = m.nb > 3 ? entry_valid(e3) : 0;
+  m.full = m.nb == 4 && m.vl0 == 16 && m.vl1 == 16 && m.vl2 == 16 && m.vl3 == 16 &&
+           (!a.causal || m.ps3 + 15 <= q_min);
 }
 
 template <int D>
@@ -104,13 +135,15 @@ struct StepRegs {
   uint4 v[D / 32];   // keys-per-thread of one 16-byte d chunk
 };
 
-// Global -> registers for one step.  Slots without a key load as zero.
+// Global -> registers for one step.  Every load is in bounds (block ids of
+// the step are pool ids, slots 0..15); slots that hold no key are dealt with
+// later (K: masked scores, V: zeroed when staged).  K and V are fetched at
+// different points of a step so that their staging registers are not live
+// at the same time.
 template <int D>
-__device__ __forceinline__ void fetch_step(const KernelArgs& a, int kv_head, const StepMeta& m,
-                                           StepRegs<D>& r, int t) {
+__device__ __forceinline__ void fetch_k(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
   const bf16_t* __restrict__ K = (const bf16_t*)a.k;
-  const bf16_t* __restrict__ V = (const bf16_t*)a.v;
   const int64_t head_off = (int64_t)kv_head * (kBlock * D);
   const int64_t blk_stride = (int64_t)a.num_kv_heads * (kBlock * D);
 #pragma unroll
@@ -120,60 +153,156 @@ __device__ __forceinline__ void fetch_step(const KernelArgs& a, int kv_head, con
     const int b = (D == 128) ? i : 2 * i + (t >> 7);
     const int slot = (D == 128) ? (t >> 4) : ((t >> 3) & 15);
     const int c = t % CPR;
-    const int phys = m.phys(b);
-    const int valid = m.valid(b);
-    const bool ok = b < m.nb && slot < valid;
-    const uint4* src = (const uint4*)(K + phys * blk_stride + head_off + slot * D + c * 8);
-    r.k[i] = ok ? *src : make_uint4(0, 0, 0, 0);
+    r.k[i] = *(const uint4*)(K + m.phys(b) * blk_stride + head_off + slot * D + c * 8);
   }
+}
+template <int D>
+__device__ __forceinline__ void fetch_v(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
+  constexpr int CPR = D / 8;
   constexpr int KPT = D / 32;            // keys per thread for V
+  const bf16_t* __restrict__ V = (const bf16_t*)a.v;
+  const int64_t head_off = (int64_t)kv_head * (kBlock * D);
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * (kBlock * D);
   const int c = t % CPR, kg = t / CPR;
-  const int kbase = kg * KPT;
-  const int b = kbase >> 4, slot0 = kbase & 15;
-  const int phys = m.phys(b);
-  const int valid = m.valid(b);
+  const int b = (kg * KPT) >> 4, slot0 = (kg * KPT) & 15;
+  const bf16_t* vsrc = V + m.phys(b) * blk_stride + head_off + slot0 * D + c * 8;
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    const bool ok = b < m.nb && slot0 + e < valid;
-    const uint4* src = (const uint4*)(V + phys * blk_stride + head_off + (slot0 + e) * D + c * 8);
-    r.v[e] = ok ? *src : make_uint4(0, 0, 0, 0);
-  }
+  for (int e = 0; e < KPT; ++e) r.v[e] = *(const uint4*)(vsrc + e * D);
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& u, int w) {
   return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
 }
 
-// Registers -> LDS buffer (K row-major swizzled, V transposed).
+// Registers -> LDS buffer: K row-major swizzled; V transposed, with V rows of
+// slots without a key written as zero on steps that are not full.
 template <int D>
-__device__ __forceinline__ void stage_step(PrefillSmem<D>& sm, int buf, const StepRegs<D>& r, int t) {
+__device__ __forceinline__ void stage_k(PrefillSmem<D>& sm, int buf, const StepRegs<D>& r, int t) {
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const int id = i * kThreads + t;
     const int row = id / CPR, c = id % CPR;
-    sm.k[buf][k_chunk<D>(row, c)] = r.k[i];
+    const int cp = c ^ k_swz<D>(row);
+    sm.k[buf][0][row][cp] = make_uint2(r.k[i].x, r.k[i].y);
+    sm.k[buf][1][row][cp] = make_uint2(r.k[i].z, r.k[i].w);
   }
+}
+template <int D>
+__device__ __forceinline__ void stage_v(PrefillSmem<D>& sm, int buf, StepRegs<D>& r, const StepMeta& m, int t) {
+  constexpr int CPR = D / 8;
   constexpr int KPT = D / 32;
   const int c = t % CPR, kg = t / CPR;
+  if (!m.full) {
+    const int b = (kg * KPT) >> 4, slot0 = (kg * KPT) & 15;
+    const int valid = b < m.nb ? m.valid(b) : 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+      if (slot0 + e >= valid) r.v[e] = make_uint4(0, 0, 0, 0);
+  }
   const int kpos = vt_key_pos(kg * KPT);
-  char* vbase = (char*)sm.vt[buf];
+  const int chunk = kpos >> 3, half = (kpos >> 2) & 1;
 #pragma unroll
   for (int dd = 0; dd < 8; ++dd) {
     const int d = c * 8 + dd;
-    const int off = vt_chunk(d, kpos >> 3) * 16 + (kpos & 7) * 2;
     const int w = dd >> 1;
-    const bool hi = dd & 1;
+    // bytes {0,1} (even dd) or {2,3} (odd dd) of word w of each key, low key first
+    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+    uint2* dst = &sm.vt[buf][half][d][chunk ^ vt_swz(d)];
     if constexpr (KPT == 4) {
-      uint32_t x0 = word_of(r.v[0], w), x1 = word_of(r.v[1], w), x2 = word_of(r.v[2], w), x3 = word_of(r.v[3], w);
-      uint2 val;
-      val.x = hi ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-      val.y = hi ? ((x2 >> 16) | (x3 & 0xffff0000u)) : ((x2 & 0xffffu) | (x3 << 16));
-      *(uint2*)(vbase + off) = val;
+      *dst = make_uint2(__builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel),
+                        __builtin_amdgcn_perm(word_of(r.v[3], w), word_of(r.v[2], w), sel));
     } else {
-      uint32_t x0 = word_of(r.v[0], w), x1 = word_of(r.v[1], w);
-      *(uint32_t*)(vbase + off) = hi ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      // 2 keys per thread: a 4-byte store into the (kpos & 3) / 2 word of the half
+      ((uint32_t*)dst)[(kpos >> 1) & 1] = __builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel);
     }
+  }
+}
+
+// Scores of one 32-row half for a step: s{kb} register r holds key
+// 32kb + 8(r/4) + 4h + r%4 (block 2kb + r/8, slot 8((r/4)&1) + 4h + r%4).
+__device__ __forceinline__ void mask_half(f32x16& s0, f32x16& s1, const StepMeta& m, int h, int qpos, bool causal) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int slot = 8 * ((r >> 2) & 1) + 4 * h + (r & 3);
+    const int b0 = r >> 3, b1 = 2 + (r >> 3);
+    const bool ok0 = slot < m.valid(b0) && (!causal || m.pos0(b0) + slot <= qpos);
+    const bool ok1 = slot < m.valid(b1) && (!causal || m.pos0(b1) + slot <= qpos);
+    s0[r] = ok0 ? s0[r] : kNegInf;
+    s1[r] = ok1 ? s1[r] : kNegInf;
+  }
+}
+
+__device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[r], s1[r]));
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+// p = exp2(s * c2 - m) rounded to bf16 in pw (word j of kb: regs 2j, 2j+1);
+// returns this lane's part of the row sum (the other lane half holds the rest).
+__device__ __forceinline__ float exp_half(const f32x16& s0, const f32x16& s1, float c2, float m_use, uint32_t (&pw)[16]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -m_use));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, -m_use));
+    const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -m_use));
+    const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, -m_use));
+    rs += (p0 + p1) + (p2 + p3);
+    pw[r / 2] = pack_bf16x2(p0, p1);
+    pw[8 + r / 2] = pack_bf16x2(p2, p3);
+  }
+  return rs;
+}
+
+struct RowInfo {
+  bool ok;
+  int token, head, qpos;
+};
+
+__device__ __forceinline__ RowInfo row_info(const KernelArgs& a, const WorkItem& it, int mrow) {
+  RowInfo ri;
+  const int g = a.group;
+  ri.ok = mrow < it.n_q * g;
+  ri.token = it.q_row0 + (ri.ok ? mrow / g : 0);
+  ri.head = it.kv_head * g + (ri.ok ? mrow % g : 0);
+  ri.qpos = ri.ok ? a.q_pos[ri.token] : INT_MIN;
+  return ri;
+}
+
+template <int D>
+__device__ __forceinline__ void write_rows(const KernelArgs& a, const WorkItem& it, const RowInfo& ri, int mrow, int h,
+                                           const f32x16 (&acc)[D / 32], float m, float l_tot) {
+  if (!ri.ok) return;
+  const bool any = l_tot > 0.f;
+  const float inv = any ? 1.f / l_tot : 0.f;
+  const float lse_v = any ? (m + log2f(l_tot)) * kLn2 : kNegInf;
+  if (it.part_row < 0) {
+    bf16_t* orow = (bf16_t*)a.out + ((int64_t)ri.token * a.num_q_heads + ri.head) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + q4 * 8 + h * 4;
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][q4 * 4 + 0] * inv, acc[db][q4 * 4 + 1] * inv);
+        w.y = pack_bf16x2(acc[db][q4 * 4 + 2] * inv, acc[db][q4 * 4 + 3] * inv);
+        *(uint2*)(orow + d0) = w;
+      }
+    if (a.lse && h == 0) a.lse[(int64_t)ri.token * a.num_q_heads + ri.head] = lse_v;
+  } else {
+    float* prow = a.part_o + (int64_t)(it.part_row + mrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + q4 * 8 + h * 4;
+        *(float4*)(prow + d0) = make_float4(acc[db][q4 * 4] * inv, acc[db][q4 * 4 + 1] * inv,
+                                            acc[db][q4 * 4 + 2] * inv, acc[db][q4 * 4 + 3] * inv);
+      }
+    if (h == 0) a.part_lse[it.part_row + mrow] = lse_v;
   }
 }
 
@@ -186,23 +315,16 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
   const int lane = t & 63;
   const int h = lane >> 5;        // lane half: which 8 of each 16 reduction indices
   const int col = lane & 31;      // tile row within the wave
-  const int g = a.group;
-  const int n_mrows = it.n_q * g;
   const int mrow = wave * 32 + col;
-  const bool row_ok = mrow < n_mrows;
-  const int token = it.q_row0 + (row_ok ? mrow / g : 0);
-  const int head = it.kv_head * g + (row_ok ? mrow % g : 0);
-  const int qpos = row_ok ? a.q_pos[token] : INT_MIN;
+  const RowInfo ri = row_info(a, it, mrow);
 
   // Q^T operand: lane holds q[row][16ks + 8h .. +8) for every ks.
   bf16x8 qop[D / 16];
   {
-    const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)token * a.num_q_heads + head) * D;
+    const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)ri.token * a.num_q_heads + ri.head) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      uint4 u = row_ok ? *(const uint4*)(qrow + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0);
-      qop[ks] = as_bf16x8(u);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      qop[ks] = as_bf16x8(ri.ok ? *(const uint4*)(qrow + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0));
   }
 
   f32x16 acc[D / 32];
@@ -216,124 +338,72 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
   if (nsteps > 0) {
     StepMeta cur, nxt;
     StepRegs<D> regs;
-    load_meta(a, it.blk_begin, it.blk_end, cur);
-    fetch_step<D>(a, it.kv_head, cur, regs, t);
-    stage_step<D>(sm, 0, regs, t);
-    if (nsteps > 1) load_meta(a, it.blk_begin + 4, it.blk_end, nxt);
+    load_meta(a, it.blk_begin, it.blk_end, it.q_min, cur);
+    fetch_k<D>(a, it.kv_head, cur, regs, t);
+    fetch_v<D>(a, it.kv_head, cur, regs, t);
+    stage_k<D>(sm, 0, regs, t);
+    stage_v<D>(sm, 0, regs, cur, t);
+    load_meta(a, it.blk_begin + 4, it.blk_end, it.q_min, nxt);
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
       const int buf = s & 1;
-      const bool more = s + 1 < nsteps;
-      if (more) fetch_step<D>(a, it.kv_head, nxt, regs, t);
+      // Next step's K (a step past the item's end reads in-bounds pool blocks
+      // and is never used).
+      fetch_k<D>(a, it.kv_head, nxt, regs, t);
 
       // ---- S^T = K Q^T for 64 keys ----
       f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
-      const uint4* kl = sm.k[buf];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 k0 = as_bf16x8(kl[k_chunk<D>(col, 2 * ks + h)]);
-        const bf16x8 k1 = as_bf16x8(kl[k_chunk<D>(32 + col, 2 * ks + h)]);
+        const bf16x8 k0 = ld_k<D>(sm, buf, col, 2 * ks + h);
+        const bf16x8 k1 = ld_k<D>(sm, buf, 32 + col, 2 * ks + h);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
       }
+      stage_k<D>(sm, buf ^ 1, regs, t);
+      fetch_v<D>(a, it.kv_head, nxt, regs, t);
 
-      // ---- mask: register r of s{kb} holds key 32kb + 8(r/4) + 4h + r%4,
-      //      i.e. block 2kb + r/8, slot 8((r/4)&1) + 4h + r%4 ----
-      const int last = cur.nb - 1;
-      const bool full = cur.nb == 4 && cur.vl0 == 16 && cur.vl1 == 16 && cur.vl2 == 16 && cur.vl3 == 16 &&
-                        (!a.causal || cur.ps3 + 15 <= it.q_min);
-      (void)last;
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int slot = 8 * ((r >> 2) & 1) + 4 * h + (r & 3);
-          const int b0 = r >> 3, b1 = 2 + (r >> 3);
-          const bool ok0 = slot < cur.valid(b0) && (!a.causal || cur.pos0(b0) + slot <= qpos);
-          const bool ok1 = slot < cur.valid(b1) && (!a.causal || cur.pos0(b1) + slot <= qpos);
-          s0[r] = ok0 ? s0[r] : kNegInf;
-          s1[r] = ok1 ? s1[r] : kNegInf;
-        }
-      }
+      if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
 
       // ---- online softmax (exp2 domain) ----
-      float mx = kNegInf;
+      // The reference max of a row only moves when the row max exceeds it by
+      // more than 2^8: exact (output and row sum share the reference), p stays
+      // <= 256, and most steps skip rescaling the accumulators.
+      const float mx = row_max(s0, s1) * c2;
+      const bool grow = mx > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // rows that keep their reference get alpha = 1 (also when it is -inf)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;  // m = -inf: 0
+        m = grow ? mx : m;
+        l *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m, mx * c2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      float rs = 0.f;
-      uint32_t pw[16];  // P in bf16, two per word: word j of kb holds regs 2j, 2j+1
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, -m_use));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -m_use));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, -m_use));
-        rs += (p0 + p1) + (p2 + p3);
-        pw[r / 2] = pack_bf16x2(p0, p1);
-        pw[8 + r / 2] = pack_bf16x2(p2, p3);
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      uint32_t pw[16];
+      l += exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
 
       // ---- O^T += V^T P^T ----
-      const uint4* vl = sm.vt[buf];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
         const bf16x8 pop = as_bf16x8(make_uint4(pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 v = as_bf16x8(vl[vt_chunk(db * 32 + col, 2 * ks + h)]);
+          const bf16x8 v = ld_vt<D>(sm, buf, db * 32 + col, 2 * ks + h);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
         }
       }
 
-      if (more) {
-        stage_step<D>(sm, buf ^ 1, regs, t);
-        cur = nxt;
-        if (s + 2 < nsteps) load_meta(a, it.blk_begin + 4 * (s + 2), it.blk_end, nxt);
-      }
+      stage_v<D>(sm, buf ^ 1, regs, nxt, t);
+      cur = nxt;
+      load_meta(a, it.blk_begin + 4 * (s + 2), it.blk_end, it.q_min, nxt);
       __syncthreads();
     }
   }
 
   // ---- epilogue ----
-  const float l_tot = l + __shfl_xor(l, 32, 64);
-  if (!row_ok) return;
-  const bool any = l_tot > 0.f;
-  const float inv = any ? 1.f / l_tot : 0.f;
-  const float lse_v = any ? (m + log2f(l_tot)) * kLn2 : kNegInf;
-  if (it.part_row < 0) {
-    bf16_t* orow = (bf16_t*)a.out + ((int64_t)token * a.num_q_heads + head) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + q4 * 8 + h * 4;
-        uint2 w;
-        w.x = pack_bf16x2(acc[db][q4 * 4 + 0] * inv, acc[db][q4 * 4 + 1] * inv);
-        w.y = pack_bf16x2(acc[db][q4 * 4 + 2] * inv, acc[db][q4 * 4 + 3] * inv);
-        *(uint2*)(orow + d0) = w;
-      }
-    if (a.lse && h == 0) a.lse[(int64_t)token * a.num_q_heads + head] = lse_v;
-  } else {
-    float* prow = a.part_o + (int64_t)(it.part_row + mrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + q4 * 8 + h * 4;
-        *(float4*)(prow + d0) = make_float4(acc[db][q4 * 4] * inv, acc[db][q4 * 4 + 1] * inv,
-                                            acc[db][q4 * 4 + 2] * inv, acc[db][q4 * 4 + 3] * inv);
-      }
-    if (h == 0) a.part_lse[it.part_row + mrow] = lse_v;
-  }
+  write_rows<D>(a, it, ri, mrow, h, acc, m, l + __shfl_xor(l, 32, 64));
 }
 
 }  // namespace
