@@ -145,6 +145,79 @@ def cpu_baseline(wl, flops_per_row, budget_s=12.0):
                       f"all their visible keys), fp64 numpy, {t:.1f} s"}
 
 
+# ---------------------------------------------------------------------------
+# profiler helpers
+# ---------------------------------------------------------------------------
+def copy_kernel_run(nbytes, reps=5):
+    """A plain device copy of nbytes (one read and one write of each byte),
+    used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def _csv_rows(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*.csv"), recursive=True) if os.path.isdir(path) else [path]
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(list(csv.DictReader(fh)))
+    return rows
+
+
+def _counter_kib(path, counter, name_part):
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(path)
+            if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", "")]
+    return sum(vals) / len(vals) if vals else None, len(vals)
+
+
+def write_report(args):
+    """Turn rocprofv3 output into a short committed summary (and a traffic record)."""
+    stats = [r for r in _csv_rows(args.stats) if "AverageNs" in r and r.get("Name") != "KERNEL_DISPATCH"]
+    lines = [f"# {args.kernel} on {args.units}", "", "Commands (run from the repository root on an MI355X):", ""]
+    for c in args.command:
+        lines.append(f"    {c}")
+    lines += ["", "## rocprofv3 --kernel-trace --stats", "",
+              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    rec = None
+    if args.fetch and args.write and args.copy_fetch and args.copy_write:
+        f_kib, nf = _counter_kib(args.fetch, "FETCH_SIZE", args.kernel)
+        w_kib, nw = _counter_kib(args.write, "WRITE_SIZE", args.kernel)
+        cf_kib, _ = _counter_kib(args.copy_fetch, "FETCH_SIZE", args.copy_kernel)
+        cw_kib, _ = _counter_kib(args.copy_write, "WRITE_SIZE", args.copy_kernel)
+        kf = args.copy_bytes / (cf_kib * 1024.0)
+        kw = args.copy_bytes / (cw_kib * 1024.0)
+        fetch_b, write_b = f_kib * 1024.0 * kf, w_kib * 1024.0 * kw
+        rec = {"kernel": args.kernel, "units": args.units, "kernel_src_sha": source_sha(KERNEL_SOURCES[args.key]),
+               "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+               "bytes_per_launch": fetch_b + write_b, "fetch_factor": kf, "write_factor": kw,
+               "raw_fetch_kib": f_kib, "raw_write_kib": w_kib, "dispatches": [nf, nw]}
+        lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+                  f"- kernel: FETCH_SIZE {f_kib:.0f} KiB, WRITE_SIZE {w_kib:.0f} KiB per dispatch "
+                  f"(mean of {nf} / {nw} dispatches)",
+                  f"- plain copy of {args.copy_bytes} bytes: FETCH_SIZE {cf_kib:.0f} KiB, WRITE_SIZE {cw_kib:.0f} KiB "
+                  f"-> scale factors {kf:.3f} (fetch), {kw:.3f} (write)",
+                  f"- scaled traffic per launch: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written "
+                  f"= {(fetch_b + write_b) / 1e6:.1f} MB",
+                  f"- kernel source sha256[:16]: {rec['kernel_src_sha']}"]
+        with open(os.path.join(ROOT, "profiles", f"{args.key}_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    if args.notes:
+        lines += ["", "## Notes", ""] + [f"- {n}" for n in args.notes]
+    with open(args.report, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {args.report}" + (" and traffic record" if rec else ""))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,11 +226,41 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], help="time one workload only (profiler runs)")
+    ap.add_argument("--copy-bytes", type=int, help="run a plain copy kernel of this size (counter calibration)")
+    ap.add_argument("--report", help="write a profile summary from rocprofv3 CSV output (no GPU needed)")
+    ap.add_argument("--key", choices=["prefill", "decode"])
+    ap.add_argument("--kernel", default="msa_prefill_kernel")
+    ap.add_argument("--units", default="")
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-kernel", default="neg_kernel")
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--notes", action="append", default=[])
     args = ap.parse_args()
+    if args.report:
+        write_report(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: MSA runs on a single MI355X here (no multi-GPU path).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_kernel_run(args.copy_bytes)
+        return
+    if args.only:
+        import kv_cache_attention_msa_amd as msa
+        import workloads as W
+        wl = W.config2() if args.only == "prefill" else W.config3()
+        kind = msa.KERNEL_PREFILL if args.only == "prefill" else msa.KERNEL_DECODE
+        ms, times, plan_ms = run_workload(wl, args.steps, args.warmup, kind)
+        k_ms, k_n = times[kind]
+        print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_avg_ms": k_ms / max(k_n, 1),
+                          "launches": k_n}), flush=True)
+        return
 
     import numpy as np
     import torch
