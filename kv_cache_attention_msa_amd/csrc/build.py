@@ -25,6 +25,7 @@ HOST_SOURCES = ["msa_plan.cpp", "msa_api.cpp"]
 HIP_SOURCES = sorted(f for f in os.listdir(HERE) if f.endswith(".hip"))
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{HERE}", "-Wall", "-Wno-unused-function"]
+COMMON += os.environ.get("MSA_EXTRA_CFLAGS", "").split()  # extra compiler flags (tuning experiments)
 # Packed fp32 ops stay off: the kernels are written for scalar fp32 VALU math.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]

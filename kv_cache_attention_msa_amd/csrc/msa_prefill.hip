@@ -36,27 +36,27 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
 
-// LDS tiles are kept as two arrays of 8-byte halves: every 16-byte MFMA
-// operand is read with two ds_read_b64 (on gfx950 64-bit LDS reads sustain
-// about twice the bytes per clock of 128-bit reads).  Half h of 16-byte chunk
-// c of a row lives in array h at the row's swizzled chunk position.
+// LDS tiles.  gfx950's LDS serves a ds_read_b128 16 lanes per clock (64 banks
+// x 4 bytes), so an operand read is conflict-free when the 16 lanes of each
+// quarter-wave hit 16 distinct 16-byte bank groups.  Operand reads touch 16
+// consecutive rows at one chunk index; the XOR swizzles below spread those
+// over all bank groups.
 template <int D>
 struct PrefillSmem {
-  uint2 k[2][2][kStepKeys][D / 8];   // [buf][half][key][chunk]: K rows (head_dim)
-  uint2 vt[2][2][D][kStepKeys / 8];  // [buf][half][d][chunk]: V transposed (64 keys)
+  uint4 k[2][kStepKeys][D / 8];   // [buf][key][chunk]: K rows (head_dim), swizzled
+  uint4 vt[2][D][kStepKeys / 8];  // [buf][d][chunk]: V transposed (64 keys), swizzled
 };
 
-// Chunk swizzles.  With 8-byte halves a row of the K array is 16 (D=128) or
-// 8 (D=64) bank pairs wide and a row of the Vt array 8 bank pairs wide; the
-// 16 lanes that LDS serves together read 16 consecutive rows at one chunk
-// index and must land on 16 distinct bank pairs.
+// K rows are 256 bytes (D=128: one row covers all banks) or 128 bytes (D=64:
+// rows of one parity share a bank half).
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   if constexpr (D == 128) return row & 15;
   else return (row >> 1) & 7;
 }
-// Vt rows: distinct positions for each parity class of 16 aligned rows
-// (operand reads), and for 8 rows spaced 8 apart (transposed writes).
+// Vt rows are 128 bytes: distinct positions for each parity class of 16
+// aligned rows (operand reads), and for 8 rows spaced 8 apart (the
+// transposed writes of one quarter-wave).
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 7; }
 
 // Position of local key k (0..63) inside a transposed V row: bits 2 and 3 of
@@ -72,29 +72,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// Operand loads.  The two 8-byte halves of one operand are 8 KiB (K, D=128)
-// or 4 KiB apart and merge into one ds_read2st64_b64 whose 4 result registers
-// are the operand in order.  The empty asm hides the relation between the
-// addresses of different operands, so that the compiler pairs the halves of
-// the same operand (and not the low halves of two operands, which then need
-// register moves).
 template <int D>
 __device__ __forceinline__ bf16x8 ld_k(const PrefillSmem<D>& sm, int buf, int row, int c) {
-  int off = (row * (D / 8) + (c ^ k_swz<D>(row))) * 8;
-  asm volatile("" : "+v"(off));
-  const char* base = (const char*)&sm.k[buf][0][0][0];
-  const uint2 lo = *(const uint2*)(base + off);
-  const uint2 hi = *(const uint2*)(base + off + kStepKeys * D);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  return as_bf16x8(sm.k[buf][row][c ^ k_swz<D>(row)]);
 }
 template <int D>
 __device__ __forceinline__ bf16x8 ld_vt(const PrefillSmem<D>& sm, int buf, int d, int c) {
-  int off = (d * (kStepKeys / 8) + (c ^ vt_swz(d))) * 8;
-  asm volatile("" : "+v"(off));
-  const char* base = (const char*)&sm.vt[buf][0][0][0];
-  const uint2 lo = *(const uint2*)(base + off);
-  const uint2 hi = *(const uint2*)(base + off + D * kStepKeys);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  return as_bf16x8(sm.vt[buf][d][c ^ vt_swz(d)]);
 }
 
 // Descriptors of one step's (up to) 4 blocks.  Plain scalar fields rather
@@ -183,9 +167,7 @@ __device__ __forceinline__ void stage_k(PrefillSmem<D>& sm, int buf, const StepR
   for (int i = 0; i < D / 32; ++i) {
     const int id = i * kThreads + t;
     const int row = id / CPR, c = id % CPR;
-    const int cp = c ^ k_swz<D>(row);
-    sm.k[buf][0][row][cp] = make_uint2(r.k[i].x, r.k[i].y);
-    sm.k[buf][1][row][cp] = make_uint2(r.k[i].z, r.k[i].w);
+    sm.k[buf][row][c ^ k_swz<D>(row)] = r.k[i];
   }
 }
 template <int D>
@@ -201,20 +183,19 @@ __device__ __forceinline__ void stage_v(PrefillSmem<D>& sm, int buf, StepRegs<D>
       if (slot0 + e >= valid) r.v[e] = make_uint4(0, 0, 0, 0);
   }
   const int kpos = vt_key_pos(kg * KPT);
-  const int chunk = kpos >> 3, half = (kpos >> 2) & 1;
+  const int chunk = kpos >> 3;
 #pragma unroll
   for (int dd = 0; dd < 8; ++dd) {
     const int d = c * 8 + dd;
     const int w = dd >> 1;
     // bytes {0,1} (even dd) or {2,3} (odd dd) of word w of each key, low key first
     const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-    uint2* dst = &sm.vt[buf][half][d][chunk ^ vt_swz(d)];
+    char* dst = (char*)&sm.vt[buf][d][chunk ^ vt_swz(d)] + (kpos & 7) * 2;
     if constexpr (KPT == 4) {
-      *dst = make_uint2(__builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel),
-                        __builtin_amdgcn_perm(word_of(r.v[3], w), word_of(r.v[2], w), sel));
+      *(uint2*)dst = make_uint2(__builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel),
+                                __builtin_amdgcn_perm(word_of(r.v[3], w), word_of(r.v[2], w), sel));
     } else {
-      // 2 keys per thread: a 4-byte store into the (kpos & 3) / 2 word of the half
-      ((uint32_t*)dst)[(kpos >> 1) & 1] = __builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel);
+      *(uint32_t*)dst = __builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel);
     }
   }
 }
@@ -354,6 +335,25 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
 
       // ---- S^T = K Q^T for 64 keys ----
       f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
+#ifdef MSA_SETPRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
+#ifdef MSA_PIPE_OPS
+      bf16x8 k0 = ld_k<D>(sm, buf, col, h), k1 = ld_k<D>(sm, buf, 32 + col, h);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 n0 = k0, n1 = k1;
+        if (ks + 1 < D / 16) {
+          n0 = ld_k<D>(sm, buf, col, 2 * (ks + 1) + h);
+          n1 = ld_k<D>(sm, buf, 32 + col, 2 * (ks + 1) + h);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
+        k0 = n0;
+        k1 = n1;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#else
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 k0 = ld_k<D>(sm, buf, col, 2 * ks + h);
@@ -361,6 +361,10 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
       }
+#endif
+#ifdef MSA_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       stage_k<D>(sm, buf ^ 1, regs, t);
       fetch_v<D>(a, it.kv_head, nxt, regs, t);
 
@@ -384,6 +388,26 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
       l += exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
 
       // ---- O^T += V^T P^T ----
+#ifdef MSA_SETPRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
+#ifdef MSA_PIPE_OPS
+      bf16x8 v = ld_vt<D>(sm, buf, col, h);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
+        const bf16x8 pop = as_bf16x8(make_uint4(pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int nks = (db + 1 < D / 32) ? ks : ks + 1, ndb = (db + 1 < D / 32) ? db + 1 : 0;
+          bf16x8 nv = v;
+          if (nks < 4) nv = ld_vt<D>(sm, buf, ndb * 32 + col, 2 * nks + h);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
+          v = nv;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#else
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
@@ -394,6 +418,10 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
         }
       }
+#endif
+#ifdef MSA_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
 
       stage_v<D>(sm, buf ^ 1, regs, nxt, t);
       cur = nxt;
