@@ -7,7 +7,8 @@
 // the 4 partial results are merged exactly (log-sum-exp) at the end.
 // Per 16-token block, per wave:
 //   * K is loaded straight into the A operand of v_mfma_f32_16x16x32_bf16
-//     (lane: key lane%16, a 64-byte run of head_dim) and S^T = K Q^T gives each
+//     (lane: key lane%16; the 4 lane groups of an instruction read a 64-byte
+//     run of each key row) and S^T = K Q^T gives each
 //     lane the scores of 4 keys for one row: the MFMA does the cross-lane
 //     reduction of the dot products;
 //   * masking (block tail, causal position), running max and exp2 happen in
@@ -16,8 +17,8 @@
 //   * V is read with fully coalesced 16-byte loads (4 keys x 256 bytes per
 //     instruction) and accumulated as fp32 FMAs: each lane owns 8 head_dim
 //     columns of every row;
-//   * loads for the wave's next block are in flight while the current one is
-//     computed (block ids and descriptors run two blocks ahead).
+//   * loads for the wave's next two blocks are in flight while the current one
+//     is computed.
 // Slots past a block's valid count are never loaded (V reads as zero there).
 #include "msa_common.h"
 
@@ -65,7 +66,9 @@ __device__ __forceinline__ void fetch_block(const KernelArgs& a, int kv_head, co
   const bool kok = key < b.valid;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int c = grp * KS + ks;  // this lane's 16-byte chunk for k-step ks
+    // this lane's 16-byte chunk for k-step ks: the 4 lane groups read one
+    // contiguous 64-byte run of each key row per instruction
+    const int c = 4 * ks + grp;
     r.k[ks] = kok ? *(const uint4*)(K + base + key * D + c * 8) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 2) void msa_decode_kernel(KernelArgs a) {
     const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)token * a.num_q_heads + head) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qop[ks] = as_bf16x8(row_ok ? *(const uint4*)(qrow + (grp * KS + ks) * 8) : make_uint4(0, 0, 0, 0));
+      qop[ks] = as_bf16x8(row_ok ? *(const uint4*)(qrow + (4 * ks + grp) * 8) : make_uint4(0, 0, 0, 0));
   }
 
   float acc[NM][8];
@@ -118,17 +121,18 @@ __global__ __launch_bounds__(kThreads, 2) void msa_decode_kernel(KernelArgs a) {
   const int nblk = it.blk_end - it.blk_begin;
   int i = wave;
   if (i < nblk) {
-    DecodeRegs<D> cur, nxt;
+    // Register ring of the wave's blocks i, i+4, i+8: two blocks are in flight
+    // while one is computed.  Indices past the item's end are clamped to its
+    // last block (in-bounds loads whose data is never used).
+    DecodeRegs<D> cur, nxt, nxt2;
     BlockMeta mc = block_meta(a, it.blk_begin + i);
     BlockMeta mn = block_meta(a, it.blk_begin + min(i + 4, nblk - 1));
+    BlockMeta mn2 = block_meta(a, it.blk_begin + min(i + 8, nblk - 1));
     fetch_block<D>(a, it.kv_head, mc, cur, lane);
+    fetch_block<D>(a, it.kv_head, mn, nxt, lane);
     for (; i < nblk; i += 4) {
-      const bool more = i + 4 < nblk;
-      BlockMeta mnn = mn;
-      if (more) {
-        fetch_block<D>(a, it.kv_head, mn, nxt, lane);
-        mnn = block_meta(a, it.blk_begin + min(i + 8, nblk - 1));
-      }
+      fetch_block<D>(a, it.kv_head, mn2, nxt2, lane);
+      const BlockMeta mn3 = block_meta(a, it.blk_begin + min(i + 12, nblk - 1));
 
       // ---- scores: S^T (keys x rows), lane holds keys 4*grp+r of row col ----
       f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -188,11 +192,11 @@ __global__ __launch_bounds__(kThreads, 2) void msa_decode_kernel(KernelArgs a) {
       }
       wave_sync_lds();
 
-      if (more) {
-        cur = nxt;
-        mc = mn;
-        mn = mnn;
-      }
+      cur = nxt;
+      nxt = nxt2;
+      mc = mn;
+      mn = mn2;
+      mn2 = mn3;
     }
   }
 
