@@ -118,6 +118,20 @@ def run_workload(wl, steps, warmup, kind):
     return wall / steps * 1e3, times, plan_ms
 
 
+def attainable_peaks():
+    """What this GPU sustains, measured by the probes of libmsa_peaks.so: a
+    streaming HBM read (4 GiB, 16 B per lane) and back-to-back bf16 MFMAs."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_attention_msa_amd", "libmsa_peaks.so"))
+    lib.msa_peak_hbm_read.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.msa_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    gbps, tflops = ctypes.c_double(), ctypes.c_double()
+    assert lib.msa_peak_hbm_read(4 << 30, 5, ctypes.byref(gbps)) == 0
+    assert lib.msa_peak_mfma_bf16(4000, ctypes.byref(tflops)) == 0
+    return {"hbm_read_GBps": gbps.value, "mfma_bf16_TFLOPs": tflops.value,
+            "how": "libmsa_peaks.so: streaming 4 GiB read; v_mfma_f32_32x32x16_bf16 loop on independent accumulators"}
+
+
 def cpu_baseline(wl, flops_per_row, budget_s=12.0):
     """The fp64 oracle on a bounded sample: whole sequences, taken in order,
     until about budget_s of CPU time has been spent."""
@@ -312,6 +326,12 @@ def main():
                          "kernel_ms": d_avg, "merge_ms": m_ms / m_n if m_n else 0.0},
         }
         del wl3
+    att = attainable_peaks()
+    line["attainable"] = att
+    roofline["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOPs"] if achieved else None
+    if "secondary" in line:
+        sr = line["secondary"]["roofline"]
+        sr["frac_of_attainable"] = sr["achieved"] / att["hbm_read_GBps"] if sr["achieved"] else None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, counts * wl.num_q_heads * 4 * wl.head_dim)
     print(json.dumps(line), flush=True)

@@ -19,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
+PEAKS_LIB = os.path.join(PKG, "libmsa_peaks.so")   # measurement probes (benchmark only)
+PEAKS_SOURCE = os.path.join(HERE, "peaks", "msa_peaks.hip")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["msa_plan.cpp", "msa_api.cpp"]
@@ -70,6 +72,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp"
+    _run([cc, "-shared"] + COMMON + DEVICE + ["-x", "hip", PEAKS_SOURCE, "-o", tmp])
+    os.replace(tmp, PEAKS_LIB)
     return LIB
 
 

@@ -1,0 +1,106 @@
+// Attainable-rate probes (see include/msa_peaks.h): a streaming HBM read and
+// a bf16 MFMA issue loop.  Measurement tooling for the benchmark only.
+#include <hip/hip_runtime.h>
+
+#include "msa_peaks.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, size_t n, uint32_t* out) {
+  uint32_t acc = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads live; practically never taken
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(float* out, int iters) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(threadIdx.x * 0.001f + i);
+    b[i] = (__bf16)(i * 0.5f);
+  }
+  f32x16 c0 = (f32x16){0}, c1 = (f32x16){0}, c2 = (f32x16){0}, c3 = (f32x16){0};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  const float s = c0[0] + c1[5] + c2[10] + c3[15];
+  if (s == 1234.5f) out[threadIdx.x] = s;
+}
+
+#define PK_HIP(x)                      \
+  do {                                 \
+    if ((x) != hipSuccess) return -5;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" int msa_peak_hbm_read(size_t bytes, int iters, double* gbps) {
+  if (!gbps || bytes == 0 || bytes % 16 || iters <= 0) return -1;
+  void* p = nullptr;
+  uint32_t* out = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = -5;
+  if (hipMalloc(&p, bytes) == hipSuccess && hipMalloc(&out, 64) == hipSuccess &&
+      hipMemset(p, 1, bytes) == hipSuccess && hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+      hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+    int dev = 0, cus = 256;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const dim3 grid(8 * cus);
+    const size_t n = bytes / 16;
+    hipLaunchKernelGGL(read_kernel, grid, dim3(256), 0, s, (const uint4*)p, n, out);
+    (void)hipEventRecord(e0, s);
+    for (int i = 0; i < iters; ++i) hipLaunchKernelGGL(read_kernel, grid, dim3(256), 0, s, (const uint4*)p, n, out);
+    (void)hipEventRecord(e1, s);
+    float ms = 0.f;
+    if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.f) {
+      *gbps = (double)bytes * iters / (ms * 1e-3) / 1e9;
+      rc = 0;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (s) (void)hipStreamDestroy(s);
+  if (out) (void)hipFree(out);
+  if (p) (void)hipFree(p);
+  return rc;
+}
+
+extern "C" int msa_peak_mfma_bf16(int iters, double* tflops) {
+  if (!tflops || iters <= 0) return -1;
+  float* out = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = -5;
+  if (hipMalloc(&out, 4096) == hipSuccess && hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+      hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+    int dev = 0, cus = 256;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int grid = 8 * cus;  // 8 work-groups of 4 waves per CU
+    hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, s, out, 10);
+    (void)hipEventRecord(e0, s);
+    hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, s, out, iters);
+    (void)hipEventRecord(e1, s);
+    float ms = 0.f;
+    if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.f) {
+      const double flops = (double)grid * 4 * iters * 4 * (2.0 * 32 * 32 * 16);
+      *tflops = flops / (ms * 1e-3) / 1e12;
+      rc = 0;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (s) (void)hipStreamDestroy(s);
+  if (out) (void)hipFree(out);
+  return rc;
+}

@@ -25,6 +25,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_peaks_library_exports_its_header():
+    import ctypes as ct
+    path = os.path.join(os.path.dirname(msa.library_path()), "libmsa_peaks.so")
+    lib = ct.CDLL(path)
+    text = open(os.path.join(os.path.dirname(HEADER), "msa_peaks.h")).read()
+    declared = set(re.findall(r"^int\s+(msa_\w+)\s*\(", text, flags=re.M))
+    assert declared == {"msa_peak_hbm_read", "msa_peak_mfma_bf16"}
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
 def _fake_pool(num_kv_heads=2, head_dim=64, dtype=msa.BF16, num_blocks=64):
     # caller-owned pointers that are never dereferenced on the host
     lib = msa.load_library()
