@@ -8,7 +8,9 @@ pool and the block table already resident in HBM.  The default workload is
 chunked prefill (4 sequences, GQA 32/8, head_dim 128, 4096-token context in 6
 scattered segments plus a 512-token chunk), reported in TFLOP/s of visible
 (query, key) pairs; the decode workload (64 sequences, 1k-8k-token contexts in
-2-16 segments over a 2M-token pool) is reported alongside in GB/s.
+2-16 segments over a 2M-token pool) is reported alongside in GB/s, and so is
+the KV write (msa_write_kv) of the mixed batch's fresh rows (16 sequences,
+61 fresh segments, 44 820 rows of 8 kv heads x 128) into its 65 536-block pool.
 
 Prints one JSON line.
 """
@@ -28,7 +30,8 @@ METRIC = "MSA attention TFLOP/s (prefill) and HBM GB/s (decode) vs MI355X roofli
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"prefill": "kv_cache_attention_msa_amd/csrc/msa_prefill.hip",
-                  "decode": "kv_cache_attention_msa_amd/csrc/msa_decode.hip"}
+                  "decode": "kv_cache_attention_msa_amd/csrc/msa_decode.hip",
+                  "write": "kv_cache_attention_msa_amd/csrc/msa_write.hip"}
 
 
 def visible_counts(wl):
@@ -116,6 +119,46 @@ def run_workload(wl, steps, warmup, kind):
     del K, V
     torch.cuda.empty_cache()
     return wall / steps * 1e3, times, plan_ms
+
+
+def run_write(wl, fresh, steps, warmup):
+    """Time msa_write_kv of the workload's fresh rows into its pool (HIP events
+    on the launch stream for the kernel, wall clock for the whole call)."""
+    import torch
+    import kv_cache_attention_msa_amd as msa
+
+    K, V = wl.dense_pool("cuda")
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K, v=V)
+    ks, vs = fresh.k.cuda(), fresh.v.cuda()
+    bt = torch.from_numpy(wl.block_table).cuda()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pool.set_option(msa.OPT_TIMING, 1)
+    pool.kernel_time(msa.KERNEL_WRITE, reset=True)
+    for _ in range(steps):
+        msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
+    torch.cuda.synchronize()
+    k_ms, k_n = pool.kernel_time(msa.KERNEL_WRITE)
+    pool.close()
+    del K, V
+    torch.cuda.empty_cache()
+    return wall / steps * 1e3, k_ms / max(k_n, 1), k_n
+
+
+def write_bytes(wl, fresh):
+    """Algorithmic bytes of one KV write: every fresh K and V row read once and
+    written once, plus one block id per destination block."""
+    import numpy as np
+    elt = 4 if wl.dtype == "fp32" else 2
+    blocks = int(np.sum(-(-fresh.segs[:, 1] // 16))) if len(fresh.segs) else 0
+    return 2.0 * 2.0 * fresh.rows * wl.num_kv_heads * wl.head_dim * elt + 4.0 * blocks
 
 
 def attainable_peaks():
@@ -240,10 +283,10 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], help="time one workload only (profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "write"], help="time one workload only (profiler runs)")
     ap.add_argument("--copy-bytes", type=int, help="run a plain copy kernel of this size (counter calibration)")
     ap.add_argument("--report", help="write a profile summary from rocprofv3 CSV output (no GPU needed)")
-    ap.add_argument("--key", choices=["prefill", "decode"])
+    ap.add_argument("--key", choices=["prefill", "decode", "write"])
     ap.add_argument("--kernel", default="msa_prefill_kernel")
     ap.add_argument("--units", default="")
     ap.add_argument("--stats")
@@ -264,6 +307,14 @@ def main():
         sys.exit(2)
     if args.copy_bytes:
         copy_kernel_run(args.copy_bytes)
+        return
+    if args.only == "write":
+        import workloads as W
+        wl = W.config5()
+        fresh = W.fresh_kv(wl, seed=5)
+        ms, k_avg, k_n = run_write(wl, fresh, args.steps, args.warmup)
+        print(json.dumps({"workload": wl.name + "_fresh", "ms_per_step": ms, "kernel_avg_ms": k_avg,
+                          "launches": k_n}), flush=True)
         return
     if args.only:
         import kv_cache_attention_msa_amd as msa
@@ -326,12 +377,28 @@ def main():
                          "kernel_ms": d_avg, "merge_ms": m_ms / m_n if m_n else 0.0},
         }
         del wl3
+        wl5 = W.config5()
+        fresh = W.fresh_kv(wl5, seed=5)
+        b5 = write_bytes(wl5, fresh)
+        ms5, k5, n5 = run_write(wl5, fresh, args.steps, args.warmup)
+        ach5 = b5 / (k5 * 1e-3) / 1e9 if n5 else None
+        line["kv_write"] = {
+            "workload": wl5.name + "_fresh", "metric": "KV write HBM GB/s", "value": b5 / (ms5 * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": ms5, "algorithmic_bytes": b5, "segments": int(len(fresh.segs)),
+            "rows": fresh.rows,
+            "roofline": {"bound": "hbm", "achieved": ach5, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": ach5 / PEAK_HBM_GBS if ach5 else None,
+                         "traffic": traffic_for("write", wl5.name + "_fresh"), "kernel": "msa_write",
+                         "kernel_ms": k5},
+        }
+        del wl5, fresh
     att = attainable_peaks()
     line["attainable"] = att
     roofline["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOPs"] if achieved else None
-    if "secondary" in line:
-        sr = line["secondary"]["roofline"]
-        sr["frac_of_attainable"] = sr["achieved"] / att["hbm_read_GBps"] if sr["achieved"] else None
+    for key in ("secondary", "kv_write"):
+        if key in line:
+            sr = line[key]["roofline"]
+            sr["frac_of_attainable"] = sr["achieved"] / att["hbm_read_GBps"] if sr["achieved"] else None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, counts * wl.num_q_heads * 4 * wl.head_dim)
     print(json.dumps(line), flush=True)

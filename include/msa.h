@@ -134,6 +134,36 @@ typedef struct {
 int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_table,
                 msa_pool* pool, void* out, float* lse, void* stream);
 
+/* ---- KV write (recompute-scatter) ------------------------------------------- */
+/* Place freshly computed K/V rows -- a prefill chunk's own tokens, or evicted
+ * blocks rebuilt on demand (abstract and section 4.1 / Figure 5 of the
+ * AsymCache / Multi-Segment Attention paper) -- into the pool blocks that
+ * their segment descriptors name, so that msa_forward then reads them like
+ * any other segment.  For segment s, token i < segs[s].len and every kv head h:
+ *   K[block_table[segs[s].bt_start + i/16]][h][i%16][:] = k_src[src_rows[s] + i][h][:]
+ * and the same for V.  pos_start and flags are not used.  Slots that no token
+ * maps to (the tail of a partial last block, every other block) keep their
+ * contents.  The copy is exact.
+ *
+ *  k_src, v_src  device [num_src_rows][num_kv_heads][head_dim], pool dtype (the
+ *                row-major output of a K/V projection); must not overlap each
+ *                other or the pool's K/V arrays (checked)
+ *  segs          host [num_segs]; len 0 is allowed (nothing written)
+ *  src_rows      host int32 [num_segs]: row of k_src/v_src holding token 0 of
+ *                segment s; 0 <= src_rows[s], src_rows[s] + len <= num_src_rows
+ *  block_table   device int32 [block_table_len], as for msa_forward; entries are
+ *                clamped into [0, num_blocks) on the device
+ *  stream        hipStream_t to enqueue on; ordered with msa_forward calls on
+ *                the same pool and stream
+ *
+ * Two segments may not use the same block-table entry (checked).  Distinct
+ * entries naming the same pool block are a caller error that is not checked
+ * (which write lands is then unspecified).
+ * Errors: INVALID_ARG, OOM, WORKSPACE (more than 2^31 (block, head) tiles), HIP. */
+int msa_write_kv(msa_pool* pool, const void* k_src, const void* v_src, int32_t num_src_rows,
+                 const msa_segment* segs, const int32_t* src_rows, int32_t num_segs,
+                 const int32_t* block_table, int32_t block_table_len, void* stream);
+
 /* Message for the last error on this thread ("" if none). */
 const char* msa_last_error(void);
 
@@ -152,6 +182,7 @@ int msa_pool_set_option(msa_pool* pool, int32_t option, int64_t value);
 #define MSA_KERNEL_FP32    2    /* fp32 kernel                                      */
 #define MSA_KERNEL_MERGE   3    /* log-sum-exp merge of split partials              */
 #define MSA_KERNEL_UPLOAD  4    /* copy of the per-call plan into device memory     */
+#define MSA_KERNEL_WRITE   5    /* KV write (msa_write_kv)                          */
 
 /* With MSA_OPT_TIMING on: total device time (ms, from HIP events recorded on
  * the launch stream around each launch) and number of launches of `kind`

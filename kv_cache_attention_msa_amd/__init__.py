@@ -15,9 +15,9 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "MsaError", "Pool", "SegDesc", "forward", "plan_debug", "library_path", "load_library",
+    "MsaError", "Pool", "SegDesc", "forward", "write_kv", "plan_debug", "library_path", "load_library",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
-    "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD",
+    "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
     "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS",
 ]
 
@@ -26,10 +26,10 @@ SEG_FRESH = 1
 BLOCK_SIZE = 16
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS = 1, 2, 3
-KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD = 0, 1, 2, 3, 4
+KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_WRITE = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
-    "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_last_error",
+    "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_write_kv", "msa_last_error",
     "msa_pool_set_option", "msa_pool_kernel_time", "msa_plan_debug",
 )
 
@@ -83,6 +83,7 @@ def load_library():
     lib.msa_pool_kv_ptrs.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P)]
     lib.msa_destroy_pool.argtypes = [P]
     lib.msa_forward.argtypes = [P, ctypes.POINTER(_SegDesc), P, P, P, P, P]
+    lib.msa_write_kv.argtypes = [P, P, P, I32, P, P, I32, P, I32, P]
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_pool_set_option.argtypes = [P, I32, I64]
@@ -198,6 +199,35 @@ def forward(q, seg_desc: SegDesc, block_table, pool: Pool, out, lse=None, stream
     """
     _check(load_library().msa_forward(_ptr(q), ctypes.byref(seg_desc.c), _ptr(block_table), pool.handle,
                                       _ptr(out), _ptr(lse), _current_stream(stream)))
+
+
+def write_kv(pool: Pool, k_src, v_src, segs, src_rows, block_table, stream=None):
+    """Enqueue the KV write of fresh rows into the pool (see msa_write_kv).
+
+    ``k_src``/``v_src``: contiguous [rows, num_kv_heads, head_dim] device
+    tensors of the pool dtype; ``segs``: int32 [n, 4] (pos_start, len,
+    bt_start, flags); ``src_rows``: int32 [n], row of each segment's token 0;
+    ``block_table``: int32 device tensor.
+    """
+    segs = np.ascontiguousarray(np.asarray(segs, dtype=np.int32).reshape(-1, 4))
+    src_rows = np.ascontiguousarray(src_rows, dtype=np.int32).reshape(-1)
+    if len(src_rows) != len(segs):
+        raise ValueError("segs and src_rows differ in length")
+    rows = 0
+    for t in (k_src, v_src):
+        if t is None:
+            continue
+        if not t.is_contiguous() or t.dim() != 3 or tuple(t.shape[1:]) != (pool.num_kv_heads, pool.head_dim):
+            raise ValueError("k_src/v_src must be contiguous [rows, num_kv_heads, head_dim]")
+        if t.element_size() != (4 if pool.dtype == FP32 else 2):
+            raise ValueError("k_src/v_src element type differs from the pool's")
+        rows = t.shape[0]
+    if k_src is not None and v_src is not None and k_src.shape != v_src.shape:
+        raise ValueError("k_src and v_src differ in shape")
+    _check(load_library().msa_write_kv(pool.handle, _ptr(k_src), _ptr(v_src), int(rows), segs.ctypes.data,
+                                       src_rows.ctypes.data, len(segs), _ptr(block_table),
+                                       int(block_table.shape[0]) if block_table is not None else 0,
+                                       _current_stream(stream)))
 
 
 def plan_debug(seg_desc: SegDesc, num_kv_heads: int, head_dim: int, dtype: int = BF16,

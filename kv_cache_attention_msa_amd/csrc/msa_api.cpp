@@ -10,13 +10,18 @@
 //      the items of each kind, then the merge kernel when some tile was split
 //      over KV.  Everything is on the caller's stream, so consecutive calls
 //      are ordered without cross-stream events.
+//
+// msa_write_kv uses the same staging and upload for its destination block
+// list, then one copy kernel that places the fresh K/V rows.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 
 #include "msa_internal.h"
 
@@ -107,6 +112,7 @@ struct msa_pool {
   int64_t launches[kNumKinds] = {};
 
   Plan plan;
+  std::vector<BlockEntry> write_entries;  // msa_write_kv's block list
 };
 
 namespace {
@@ -210,6 +216,37 @@ int ensure_stage(msa_pool* p, int slot, size_t bytes) {
 }
 
 size_t elem_size(int dtype) { return dtype == MSA_FP32 ? 4 : 2; }
+
+// Packs `bytes` of per-call data (written by `fill` into host memory) into
+// the next staging slot and enqueues its copy into the device plan buffer on
+// `stream`; the first n_blocks BlockEntry of the data get their block-table
+// index resolved to a pool block id on the way.
+template <typename Fill>
+int stage_and_upload(msa_pool* p, hipStream_t stream, size_t bytes, int32_t n_blocks,
+                     const int32_t* block_table, Fill&& fill) {
+  int rc = ensure_device(p, &p->d_plan, &p->plan_cap, bytes, stream, "plan buffer");
+  if (rc) return rc;
+  const int slot = p->next_slot;
+  p->next_slot = (p->next_slot + 1) % msa_pool::kSlots;
+  rc = ensure_stage(p, slot, bytes);
+  if (rc) return rc;
+  fill((char*)p->h_stage[slot]);
+  rc = timed_launch(p, kUpload, stream, [&]() {
+    return launch_upload(p->h_stage_dev[slot], p->d_plan, bytes, n_blocks, block_table, p->desc.num_blocks,
+                         stream);
+  });
+  if (rc) return rc;
+  MSA_HIP(hipEventRecord(p->stage_done[slot], stream));
+  p->stage_pending[slot] = true;
+  p->used = true;
+  p->last_stream = stream;
+  return MSA_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
 
 }  // namespace
 
@@ -423,31 +460,17 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
     rc = ensure_device(p, &p->d_part, &p->part_bytes, part_need, stream, "partial-result buffer");
     if (rc) return rc;
   }
-  rc = ensure_device(p, &p->d_plan, &p->plan_cap, plan_bytes, stream, "plan buffer");
-  if (rc) return rc;
-  const int slot = p->next_slot;
-  p->next_slot = (p->next_slot + 1) % msa_pool::kSlots;
-  rc = ensure_stage(p, slot, plan_bytes);
-  if (rc) return rc;
-  char* h = (char*)p->h_stage[slot];
-  if (!plan.blocks.empty()) memcpy(h + off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
-  memset(h + off_blocks + plan.blocks.size() * sizeof(BlockEntry), 0, kBlockPad * sizeof(BlockEntry));
-  memcpy(h + off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
-  for (int k = 0; k < 3; ++k)
-    if (!plan.items[k].empty())
-      memcpy(h + off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
-  if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
-
-  char* dws = (char*)p->d_plan;
-  rc = timed_launch(p, kUpload, stream, [&]() {
-    return launch_upload(p->h_stage_dev[slot], dws, plan_bytes, (int32_t)plan.blocks.size(), block_table,
-                         p->desc.num_blocks, stream);
+  rc = stage_and_upload(p, stream, plan_bytes, (int32_t)plan.blocks.size(), block_table, [&](char* h) {
+    if (!plan.blocks.empty()) memcpy(h + off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
+    memset(h + off_blocks + plan.blocks.size() * sizeof(BlockEntry), 0, kBlockPad * sizeof(BlockEntry));
+    memcpy(h + off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
+    for (int k = 0; k < 3; ++k)
+      if (!plan.items[k].empty())
+        memcpy(h + off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
+    if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
   });
   if (rc) return rc;
-  MSA_HIP(hipEventRecord(p->stage_done[slot], stream));
-  p->stage_pending[slot] = true;
-  p->used = true;
-  p->last_stream = stream;
+  char* dws = (char*)p->d_plan;
 
   // ---- launches ----
   KernelArgs a{};
@@ -489,6 +512,83 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
     if (rc) return rc;
   }
   return MSA_OK;
+}
+
+int msa_write_kv(msa_pool* p, const void* k_src, const void* v_src, int32_t num_src_rows, const msa_segment* segs,
+                 const int32_t* src_rows, int32_t num_segs, const int32_t* block_table, int32_t block_table_len,
+                 void* stream_) {
+  // ---- host-side checks (no HIP call before they pass) ----
+  if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
+  if (num_segs < 0 || num_src_rows < 0 || block_table_len < 0)
+    return set_error(MSA_ERR_INVALID_ARG, "num_segs, num_src_rows and block_table_len must be >= 0");
+  if (num_segs > 0 && (!segs || !src_rows)) return set_error(MSA_ERR_INVALID_ARG, "segs or src_rows is NULL");
+  std::vector<std::pair<int32_t, int32_t>> bt_ranges;  // [bt_start, bt_end) of non-empty segments
+  bt_ranges.reserve(num_segs);
+  int64_t n_entries = 0;
+  for (int32_t s = 0; s < num_segs; ++s) {
+    const msa_segment& g = segs[s];
+    if (g.len < 0 || g.bt_start < 0 || src_rows[s] < 0)
+      return set_error(MSA_ERR_INVALID_ARG, "segment %d: len, bt_start and src_rows must be >= 0", s);
+    if (g.len == 0) continue;
+    const int64_t nb = (g.len + kBlock - 1) / kBlock;
+    if ((int64_t)g.bt_start + nb > block_table_len)
+      return set_error(MSA_ERR_INVALID_ARG, "segment %d: block-table range [%d, %lld) exceeds block_table_len %d", s,
+                       g.bt_start, (long long)(g.bt_start + nb), block_table_len);
+    if ((int64_t)src_rows[s] + g.len > num_src_rows)
+      return set_error(MSA_ERR_INVALID_ARG, "segment %d: source rows [%d, %lld) exceed num_src_rows %d", s,
+                       src_rows[s], (long long)src_rows[s] + g.len, num_src_rows);
+    bt_ranges.emplace_back(g.bt_start, (int32_t)(g.bt_start + nb));
+    n_entries += nb;
+  }
+  std::sort(bt_ranges.begin(), bt_ranges.end());
+  for (size_t i = 1; i < bt_ranges.size(); ++i)
+    if (bt_ranges[i].first < bt_ranges[i - 1].second)
+      return set_error(MSA_ERR_INVALID_ARG, "two segments share block-table entry %d", bt_ranges[i].first);
+  if (n_entries == 0) return MSA_OK;
+  if (block_table_len > kMaxPoolBlocks)
+    return set_error(MSA_ERR_WORKSPACE, "block_table_len %d exceeds %d", block_table_len, kMaxPoolBlocks);
+  const int64_t n_tasks = n_entries * p->desc.num_kv_heads;
+  if (n_tasks > INT32_MAX) return set_error(MSA_ERR_WORKSPACE, "%lld (block, head) tiles exceed 2^31", (long long)n_tasks);
+  if (!k_src || !v_src || !block_table) return set_error(MSA_ERR_INVALID_ARG, "k_src, v_src or block_table is NULL");
+  const size_t row_bytes = (size_t)p->desc.head_dim * elem_size(p->desc.dtype);
+  const size_t src_bytes = (size_t)num_src_rows * p->desc.num_kv_heads * row_bytes;
+  const size_t pool_bytes = (size_t)p->desc.num_blocks * p->desc.num_kv_heads * kBlock * row_bytes;
+  if (ranges_overlap(k_src, src_bytes, v_src, src_bytes) || ranges_overlap(k_src, src_bytes, p->k, pool_bytes) ||
+      ranges_overlap(k_src, src_bytes, p->v, pool_bytes) || ranges_overlap(v_src, src_bytes, p->k, pool_bytes) ||
+      ranges_overlap(v_src, src_bytes, p->v, pool_bytes))
+    return set_error(MSA_ERR_INVALID_ARG, "k_src and v_src must not overlap each other or the pool");
+
+  // ---- block list: one entry per destination block, pos0 = source row of slot 0 ----
+  std::vector<BlockEntry>& ent = p->write_entries;
+  ent.clear();
+  ent.reserve((size_t)n_entries);
+  for (int32_t s = 0; s < num_segs; ++s) {
+    const msa_segment& g = segs[s];
+    for (int32_t j = 0; j * kBlock < g.len; ++j) {
+      const int32_t valid = std::min(kBlock, g.len - j * kBlock);
+      ent.push_back(BlockEntry{(int32_t)((uint32_t)(g.bt_start + j) | ((uint32_t)(valid - 1) << kBtIndexBits)),
+                               src_rows[s] + j * kBlock});
+    }
+  }
+
+  hipStream_t stream = (hipStream_t)stream_;
+  DeviceGuard guard(p->desc.device);
+  if (!guard.ok) return set_error(MSA_ERR_HIP, "cannot select device %d", p->desc.device);
+  const size_t bytes = align_up(ent.size() * sizeof(BlockEntry), 256);
+  int rc = stage_and_upload(p, stream, bytes, (int32_t)ent.size(), block_table, [&](char* h) {
+    memcpy(h, ent.data(), ent.size() * sizeof(BlockEntry));
+    memset(h + ent.size() * sizeof(BlockEntry), 0, bytes - ent.size() * sizeof(BlockEntry));
+  });
+  if (rc) return rc;
+  WriteArgs a{};
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k = p->k;
+  a.v = p->v;
+  a.blocks = (const BlockEntry*)p->d_plan;
+  a.n_tasks = (int32_t)n_tasks;
+  a.num_kv_heads = p->desc.num_kv_heads;
+  return timed_launch(p, kWrite, stream, [&]() { return launch_write(a, (int)row_bytes, stream); });
 }
 
 }  // extern "C"

@@ -54,7 +54,7 @@ struct MergeItem {
 
 enum Kind { kPrefill = MSA_KERNEL_PREFILL, kDecode = MSA_KERNEL_DECODE,
             kFp32 = MSA_KERNEL_FP32, kMerge = MSA_KERNEL_MERGE, kUpload = MSA_KERNEL_UPLOAD,
-            kNumKinds = 5 };
+            kWrite = MSA_KERNEL_WRITE, kNumKinds = 6 };
 
 struct Plan {
   std::vector<BlockEntry> blocks;
@@ -102,11 +102,25 @@ struct KernelArgs {
   int32_t max_mrows;      // largest n_q * group among the launch's items
 };
 
-// Launchers (msa_kernels.hip).  Return a hipError_t value.
+// KV write launch: one task per (block-list entry, kv head).  Entry e's pos0
+// holds the source row of its slot 0 (not a position).
+struct WriteArgs {
+  const void* k_src;      // [rows][num_kv_heads][head_dim]
+  const void* v_src;
+  void* k;                // pool
+  void* v;
+  const BlockEntry* blocks;
+  int32_t n_tasks;        // entries * num_kv_heads
+  int32_t num_kv_heads;
+};
+
+// Launchers (one per kernel source).  Return a hipError_t value.
 int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
 int launch_decode(const KernelArgs& a, int head_dim, void* stream);
 int launch_fp32(const KernelArgs& a, int head_dim, void* stream);
 int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream);
+// row_bytes = head_dim * element size: 128, 256 or 512.
+int launch_write(const WriteArgs& a, int row_bytes, void* stream);
 // Copies `bytes` (a multiple of 16) of plan from device-mapped pinned host
 // memory to `dst`, resolving the first `n_blocks` entries (the block list)
 // through `block_table`; ids outside [0, num_blocks) are clamped into range.

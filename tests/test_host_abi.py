@@ -270,3 +270,38 @@ def test_planner_split_alignment():
     for it in pre:
         starts = {x["blk_begin"] for x in pre if x["q_row0"] == it["q_row0"]}
         assert all((s - min(starts)) % 4 == 0 for s in starts)
+
+
+def _write(h, segs, src_rows, n_rows=100, bt_len=32, k=0x10000000, v=0x20000000, bt=0x2000):
+    lib = msa.load_library()
+    segs = np.ascontiguousarray(np.asarray(segs, dtype=np.int32).reshape(-1, 4))
+    src = np.ascontiguousarray(src_rows, dtype=np.int32)
+    return lib.msa_write_kv(h, k, v, n_rows, segs.ctypes.data if len(segs) else None,
+                            src.ctypes.data if len(src) else None, len(segs), bt, bt_len, 0)
+
+
+def test_write_kv_argument_checks():
+    """Every msa_write_kv check runs before a HIP call, so these need no GPU."""
+    h = _fake_pool()
+    lib = msa.load_library()
+    E = msa.ERR_INVALID_ARG
+    try:
+        assert _write(h, [], []) == msa.OK                                  # nothing to write
+        assert _write(h, [(0, 0, 0, 1)], [0]) == msa.OK                     # only empty segments
+        assert _write(h, [(0, -1, 0, 1)], [0]) == E                         # negative len
+        assert _write(h, [(0, 5, -1, 1)], [0]) == E                         # negative bt_start
+        assert _write(h, [(0, 5, 0, 1)], [-1]) == E                         # negative source row
+        assert _write(h, [(0, 33, 30, 1)], [0]) == E                        # bt range 30..33 > 32 entries
+        assert _write(h, [(0, 20, 0, 1)], [81]) == E                        # rows 81..101 > 100
+        assert _write(h, [(0, 20, 0, 1), (50, 5, 1, 1)], [0, 40]) == E      # both use bt entry 1
+        assert _write(h, [(0, 20, 0, 1)], [0], k=0) == E                    # null source
+        assert _write(h, [(0, 20, 0, 1)], [0], bt=0) == E                   # null block table
+        assert _write(h, [(0, 20, 0, 1)], [0], v=0x10000000) == E           # k_src == v_src
+        assert _write(h, [(0, 20, 0, 1)], [0], k=0x18000) == E              # source inside the pool
+        assert lib.msa_write_kv(None, 1, 2, 10, None, None, 0, 3, 4, 0) == E
+        assert lib.msa_write_kv(h, 1, 2, 10, None, None, 1, 3, 4, 0) == E   # segs NULL with num_segs 1
+        assert lib.msa_write_kv(h, 1, 2, -1, None, None, 0, 3, 4, 0) == E
+        assert _write(h, [(0, 20, 0, 1), (50, 5, 1, 1)], [0, 40]) == E
+        assert "block-table entry 1" in lib.msa_last_error().decode()
+    finally:
+        lib.msa_destroy_pool(h)

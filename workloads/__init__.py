@@ -326,6 +326,41 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
 # --------------------------------------------------------------------------
+# fresh K/V rows for the KV write (recompute-scatter)
+# --------------------------------------------------------------------------
+@dataclass
+class FreshKV:
+    segs: np.ndarray       # [n, 4] int32: the workload's fresh segments, descriptor order
+    src_rows: np.ndarray   # [n] int32: row of each segment's token 0 in k / v
+    k: torch.Tensor        # [rows, H_kv, d] (CPU, workload dtype)
+    v: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return int(self.k.shape[0])
+
+
+def fresh_kv(wl, seed=0, kvscale=0.5):
+    """Newly computed K/V rows for every segment of ``wl`` flagged fresh
+    (recomputed after eviction, or a chunk's own tokens), laid out as a K/V
+    projection writes them: ``[rows, H_kv, d]``, one segment's tokens on
+    consecutive rows.  The segments' row ranges follow a random order, so
+    source order is not pool order; values are N(0,1) * kvscale rounded to the
+    workload dtype (new values, unlike the pool's)."""
+    rng = np.random.default_rng(seed)
+    fresh = np.ascontiguousarray(wl.segs[(wl.segs[:, 3] & SEG_FRESH) != 0], dtype=np.int32).reshape(-1, 4)
+    src_rows = np.zeros(len(fresh), dtype=np.int32)
+    row = 0
+    for i in rng.permutation(len(fresh)):
+        src_rows[i] = row
+        row += int(fresh[i, 1])
+    shape = (row, wl.num_kv_heads, wl.head_dim)
+    k = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(kvscale)).to(wl.torch_dtype)
+    v = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(kvscale)).to(wl.torch_dtype)
+    return FreshKV(segs=fresh, src_rows=src_rows, k=k, v=v)
+
+
+# --------------------------------------------------------------------------
 # small custom cases (parity edge cases)
 # --------------------------------------------------------------------------
 def custom(seqs, *, H_q=4, H_kv=2, d=64, dtype="bf16", num_blocks=None, seed=0,
