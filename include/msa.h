@@ -159,7 +159,8 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
  * Two segments may not use the same block-table entry (checked).  Distinct
  * entries naming the same pool block are a caller error that is not checked
  * (which write lands is then unspecified).
- * Errors: INVALID_ARG, OOM, WORKSPACE (more than 2^31 (block, head) tiles), HIP. */
+ * Errors: INVALID_ARG, OOM, WORKSPACE (block_table_len above 2^28, or more
+ * than 2^31 (block, kv head) tiles), HIP. */
 int msa_write_kv(msa_pool* pool, const void* k_src, const void* v_src, int32_t num_src_rows,
                  const msa_segment* segs, const int32_t* src_rows, int32_t num_segs,
                  const int32_t* block_table, int32_t block_table_len, void* stream);

@@ -21,6 +21,11 @@ extern "C" {
  * per lane per load, `iters` timed passes; *gbps = bytes * iters / time. */
 int msa_peak_hbm_read(size_t bytes, int iters, double* gbps);
 
+/* Device-to-device copy of `bytes` (multiple of 16, > 0), 16 bytes per lane,
+ * non-temporal stores, `iters` timed passes; *gbps counts each byte once read and once written:
+ * 2 * bytes * iters / time. */
+int msa_peak_hbm_copy(size_t bytes, int iters, double* gbps);
+
 /* v_mfma_f32_32x32x16_bf16 issued back to back on independent accumulators by
  * every wave of a full-device grid, operands in registers, `iters` loop trips;
  * *tflops = dense bf16 FLOPs / time. */

@@ -547,8 +547,8 @@ int msa_write_kv(msa_pool* p, const void* k_src, const void* v_src, int32_t num_
   if (n_entries == 0) return MSA_OK;
   if (block_table_len > kMaxPoolBlocks)
     return set_error(MSA_ERR_WORKSPACE, "block_table_len %d exceeds %d", block_table_len, kMaxPoolBlocks);
-  const int64_t n_tasks = n_entries * p->desc.num_kv_heads;
-  if (n_tasks > INT32_MAX) return set_error(MSA_ERR_WORKSPACE, "%lld (block, head) tiles exceed 2^31", (long long)n_tasks);
+  if (n_entries * p->desc.num_kv_heads > INT32_MAX)
+    return set_error(MSA_ERR_WORKSPACE, "%lld (block, head) tiles exceed 2^31", (long long)(n_entries * p->desc.num_kv_heads));
   if (!k_src || !v_src || !block_table) return set_error(MSA_ERR_INVALID_ARG, "k_src, v_src or block_table is NULL");
   const size_t row_bytes = (size_t)p->desc.head_dim * elem_size(p->desc.dtype);
   const size_t src_bytes = (size_t)num_src_rows * p->desc.num_kv_heads * row_bytes;
@@ -586,7 +586,7 @@ int msa_write_kv(msa_pool* p, const void* k_src, const void* v_src, int32_t num_
   a.k = p->k;
   a.v = p->v;
   a.blocks = (const BlockEntry*)p->d_plan;
-  a.n_tasks = (int32_t)n_tasks;
+  a.n_entries = (int32_t)ent.size();
   a.num_kv_heads = p->desc.num_kv_heads;
   return timed_launch(p, kWrite, stream, [&]() { return launch_write(a, (int)row_bytes, stream); });
 }

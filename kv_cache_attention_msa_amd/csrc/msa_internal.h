@@ -102,7 +102,7 @@ struct KernelArgs {
   int32_t max_mrows;      // largest n_q * group among the launch's items
 };
 
-// KV write launch: one task per (block-list entry, kv head).  Entry e's pos0
+// KV write launch: one wave per (block-list entry, kv head).  Entry e's pos0
 // holds the source row of its slot 0 (not a position).
 struct WriteArgs {
   const void* k_src;      // [rows][num_kv_heads][head_dim]
@@ -110,7 +110,7 @@ struct WriteArgs {
   void* k;                // pool
   void* v;
   const BlockEntry* blocks;
-  int32_t n_tasks;        // entries * num_kv_heads
+  int32_t n_entries;
   int32_t num_kv_heads;
 };
 
