@@ -289,6 +289,62 @@ def write_report(args):
     print(f"wrote {args.report}" + (" and traffic record" if rec else ""))
 
 
+def latency_model_run(args):
+    """Calibrate the Eq. 5 latency model on this GPU and check its dT_B against
+    directly measured differences T(l1, q1 + D, l2 - D, q2) - T(l1, q1, l2, q2)."""
+    import numpy as np
+    from kv_cache_attention_msa_amd import calibrate as C
+
+    D = 16
+    bases = [(128, 8, 128, 8), (256, 32, 64, 8), (64, 0, 256, 32), (0, 16, 128, 1), (256, 8, 256, 1)]
+    pairs = [p for b in bases for p in (b, (b[0], b[1] + D, b[2] - D, b[3]))]
+    t0 = time.perf_counter()
+    B = args.latency_batch
+    grid = C.measure_grid(batch=B, reps=15, warmup=3, seed=1)
+    check = C.measure_grid(grid={"l1": (), "q1": (), "l2": (), "q2": ()}, batch=B, reps=41, warmup=5, seed=2,
+                           extra_points=pairs)
+    model = C.calibrate(grid)
+    rows = []
+    for i, b in enumerate(bases):
+        t_base, t_moved = check[2 * i, 4], check[2 * i + 1, 4]
+        predicted = sum(model.delta_b(b[0], b[1] + j) for j in range(D))
+        rows.append({"l1": b[0], "q1": b[1], "l2": b[2], "q2": b[3], "T_us": t_base, "T_moved_us": t_moved,
+                     "measured_dT_us": t_moved - t_base, "eq5_dT_us": predicted,
+                     "model_T_us": model(*b)})
+    res = {"model": "T = k1 + k2 (q1+q2) + k3 (l1+l2) + k4 q2 (l1+q1+l2+q2) + k5 q1 (l1+q1), sizes in 16-token blocks, T in us",
+           "workload": f"{B} requests, GQA 32/8, d 128, bf16; step = msa_write_kv of the q1+q2 fresh blocks + msa_forward "
+                       "of their query rows; median of 15 (grid) / 41 (checks) HIP-event timed steps",
+           "k": model.k, "rms_rel": model.rms, "n": int(len(grid)), "dT_check_blocks_moved": D, "checks": rows,
+           "grid": grid.tolist(), "seconds": time.perf_counter() - t0}
+    print(json.dumps({k: v for k, v in res.items() if k != "grid"}), flush=True)
+    if args.latency_out:
+        with open(args.latency_out, "w") as fh:
+            json.dump(res, fh)
+
+
+def latency_report(src, dst, command):
+    """Short text summary of a latency-model run (no GPU needed)."""
+    res = json.load(open(src))
+    k = res["k"]
+    lines = ["# Eq. 5 latency model on one MI355X", "", "Commands (run from the repository root on an MI355X):", "",
+             f"    {command}",
+             f"    python bench.py --latency-report {src} --report {dst}", "",
+             f"Model: {res['model']}.", "", f"Workload: {res['workload']}.", "",
+             "## Fitted coefficients (least squares, residuals relative to T)", "",
+             "| k1 (us) | k2 (us/block) | k3 (us/block) | k4 (us/block^2) | k5 (us/block^2) | rms rel. residual | samples |",
+             "|---|---|---|---|---|---|---|",
+             f"| {k[0]:.3f} | {k[1]:.4f} | {k[2]:.5f} | {k[3]:.3e} | {k[4]:.3e} | {res['rms_rel']:.3f} | {res['n']} |",
+             "", f"## dT_B: moving {res['dT_check_blocks_moved']} blocks from l2 to q1", "",
+             "| l1 | q1 | l2 | q2 | T measured (us) | T model (us) | dT measured (us) | dT from Eq. 5 (us) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in res["checks"]:
+        lines.append(f"| {r['l1']} | {r['q1']} | {r['l2']} | {r['q2']} | {r['T_us']:.1f} | {r['model_T_us']:.1f} | "
+                     f"{r['measured_dT_us']:.1f} | {r['eq5_dT_us']:.1f} |")
+    with open(dst, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {dst}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,7 +367,15 @@ def main():
     ap.add_argument("--copy-kernel", default="neg_kernel")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--notes", action="append", default=[])
+    ap.add_argument("--latency-model", action="store_true", help="calibrate the Eq. 5 latency model on this GPU")
+    ap.add_argument("--latency-out", help="with --latency-model: also write the full result (JSON) here")
+    ap.add_argument("--latency-batch", type=int, default=16, help="requests per step for --latency-model")
+    ap.add_argument("--latency-report", help="summarise a --latency-out JSON into --report (no GPU needed)")
     args = ap.parse_args()
+    if args.latency_report:
+        latency_report(args.latency_report, args.report,
+                       args.command[0] if args.command else f"python bench.py --latency-model --latency-out {args.latency_report}")
+        return
     if args.report:
         write_report(args)
         return
@@ -321,6 +385,9 @@ def main():
         sys.exit(2)
     if args.copy_bytes:
         copy_kernel_run(args.copy_bytes)
+        return
+    if args.latency_model:
+        latency_model_run(args)
         return
     if args.only == "write":
         import workloads as W

@@ -16,6 +16,7 @@ import numpy as np
 
 __all__ = [
     "MsaError", "Pool", "SegDesc", "forward", "write_kv", "plan_debug", "library_path", "load_library",
+    "LatencyModel", "latency_fit",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
     "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS",
@@ -31,6 +32,7 @@ KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_
 EXPORTED_SYMBOLS = (
     "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_write_kv", "msa_last_error",
     "msa_pool_set_option", "msa_pool_kernel_time", "msa_plan_debug",
+    "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b",
 )
 
 _ERR_NAMES = {ERR_INVALID_ARG: "INVALID_ARG", ERR_UNSUPPORTED: "UNSUPPORTED", ERR_OOM: "OOM",
@@ -56,6 +58,11 @@ class _SegDesc(ctypes.Structure):
                 ("seg_offsets", ctypes.c_void_p), ("segs", ctypes.c_void_p),
                 ("block_table_len", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("causal", ctypes.c_int32)]
+
+
+class _LatencyModel(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_double * 5), ("rms", ctypes.c_double), ("n", ctypes.c_int32),
+                ("relative", ctypes.c_int32)]
 
 
 PLAN_ITEM_DTYPE = np.dtype([("kind", "<i4"), ("seq", "<i4"), ("kv_head", "<i4"), ("q_row0", "<i4"),
@@ -90,6 +97,10 @@ def load_library():
     lib.msa_pool_kernel_time.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
     lib.msa_plan_debug.argtypes = [ctypes.POINTER(_SegDesc), I32, I32, I32, I32, I32, P, I32,
                                    ctypes.POINTER(I32), P, I32, ctypes.POINTER(I32)]
+    D = ctypes.c_double
+    lib.msa_latency_fit.argtypes = [P, I32, I32, ctypes.POINTER(_LatencyModel)]
+    lib.msa_latency_eval.argtypes = [ctypes.POINTER(_LatencyModel), D, D, D, D, ctypes.POINTER(D)]
+    lib.msa_latency_delta_b.argtypes = [ctypes.POINTER(_LatencyModel), D, D, ctypes.POINTER(D)]
     for name in EXPORTED_SYMBOLS:
         if name != "msa_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -228,6 +239,39 @@ def write_kv(pool: Pool, k_src, v_src, segs, src_rows, block_table, stream=None)
                                        src_rows.ctypes.data, len(segs), _ptr(block_table),
                                        int(block_table.shape[0]) if block_table is not None else 0,
                                        _current_stream(stream)))
+
+
+class LatencyModel:
+    """A fitted Eq. 5 latency model (see include/msa_latency.h); sizes in blocks."""
+
+    def __init__(self, c: _LatencyModel):
+        self.c = c
+
+    @property
+    def k(self):
+        return list(self.c.k)
+
+    @property
+    def rms(self) -> float:
+        return self.c.rms
+
+    def __call__(self, l1, q1, l2, q2) -> float:
+        t = ctypes.c_double()
+        _check(load_library().msa_latency_eval(ctypes.byref(self.c), l1, q1, l2, q2, ctypes.byref(t)))
+        return t.value
+
+    def delta_b(self, l1, q1) -> float:
+        t = ctypes.c_double()
+        _check(load_library().msa_latency_delta_b(ctypes.byref(self.c), l1, q1, ctypes.byref(t)))
+        return t.value
+
+
+def latency_fit(samples, relative: bool = True) -> LatencyModel:
+    """Fit k1..k5 to rows (l1, q1, l2, q2, T) (host only)."""
+    s = np.ascontiguousarray(np.asarray(samples, dtype=np.float64).reshape(-1, 5))
+    m = _LatencyModel()
+    _check(load_library().msa_latency_fit(s.ctypes.data, len(s), int(bool(relative)), ctypes.byref(m)))
+    return LatencyModel(m)
 
 
 def plan_debug(seg_desc: SegDesc, num_kv_heads: int, head_dim: int, dtype: int = BF16,

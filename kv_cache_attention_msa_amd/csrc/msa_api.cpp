@@ -73,6 +73,11 @@ struct TimingRecord {
 
 }  // namespace
 
+namespace msa {
+// Error reporting for the library's other host sources.
+int set_error_msg(int code, const std::string& msg) { return set_error(code, "%s", msg.c_str()); }
+}  // namespace msa
+
 struct msa_pool {
   msa_pool_desc desc{};
   void* k = nullptr;

@@ -1,0 +1,55 @@
+"""The native Eq. 5 latency-model fitter (libmsa, host only) against the CPU oracle."""
+import itertools
+
+import numpy as np
+import pytest
+
+import kv_cache_attention_msa_amd as msa
+from oracle.latency_oracle import delta_b, fit_latency, latency
+
+
+def _grid():
+    return np.array(list(itertools.product([0, 16, 64, 256], [0, 8, 32], [0, 16, 128], [4, 32])), dtype=np.float64)
+
+
+@pytest.mark.parametrize("relative", [True, False])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fit_matches_oracle_on_noisy_samples(seed, relative):
+    rng = np.random.default_rng(seed)
+    k = np.array([20.0, 0.5, 0.04, 0.002, 0.003]) * rng.uniform(0.5, 2.0, size=5)
+    g = _grid()
+    T = latency(k, *g.T) * (1 + 0.02 * rng.standard_normal(len(g)))
+    samples = np.column_stack([g, T])
+    ref, ref_rms = fit_latency(samples, relative=relative)
+    m = msa.latency_fit(samples, relative=relative)
+    np.testing.assert_allclose(m.k, ref, rtol=1e-8, atol=1e-12 * np.abs(ref).max())
+    assert m.rms == pytest.approx(ref_rms, rel=1e-8)
+    for l1, q1, l2, q2 in g[::7]:
+        assert m(l1, q1, l2, q2) == pytest.approx(latency(m.k, l1, q1, l2, q2), rel=1e-12)
+        assert m.delta_b(l1, q1) == pytest.approx(float(delta_b(m.k, l1, q1)), rel=1e-12, abs=1e-12)
+
+
+def test_exact_recovery_native():
+    k = np.array([12.0, 0.8, 0.05, 0.003, 0.004])
+    g = _grid()
+    m = msa.latency_fit(np.column_stack([g, latency(k, *g.T)]))
+    np.testing.assert_allclose(m.k, k, rtol=1e-9)
+    assert m.rms < 1e-10
+
+
+def test_bad_inputs():
+    g = _grid()
+    T = latency([1, 1, 1, 1, 1], *g.T)
+    with pytest.raises(msa.MsaError, match="determine"):
+        msa.latency_fit(np.column_stack([g, T])[g[:, 1] == 0])      # no q1 > 0: k5 unseen
+    with pytest.raises(msa.MsaError):
+        msa.latency_fit(np.ones((4, 5)))                            # too few samples
+    bad = np.column_stack([g, T])
+    bad[3, 0] = -1
+    with pytest.raises(msa.MsaError):
+        msa.latency_fit(bad)
+    bad = np.column_stack([g, T])
+    bad[5, 4] = 0.0
+    with pytest.raises(msa.MsaError):
+        msa.latency_fit(bad, relative=True)                         # relative needs T > 0
+    msa.latency_fit(bad, relative=False)                            # fine without
