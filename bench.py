@@ -311,10 +311,20 @@ def latency_model_run(args):
         rows.append({"l1": b[0], "q1": b[1], "l2": b[2], "q2": b[3], "T_us": t_base, "T_moved_us": t_moved,
                      "measured_dT_us": t_moved - t_base, "eq5_dT_us": predicted,
                      "model_T_us": model(*b)})
+    # adaptive chunk rule: chunk chosen from the model for a step-time budget, then timed
+    import kv_cache_attention_msa_amd as msa
+    chunk_cases = [(l1, q1, l2, budget) for (l1, q1, l2) in ((256, 0, 0), (128, 16, 128), (64, 32, 256))
+                   for budget in (250.0, 500.0, 1000.0)]
+    chosen = [(l1, q1, l2, msa.chunk_blocks(model, l1, q1, l2, 512, budget)) for l1, q1, l2, budget in chunk_cases]
+    timed = C.measure_grid(grid={"l1": (), "q1": (), "l2": (), "q2": ()}, batch=B, reps=21, warmup=3, seed=4,
+                           extra_points=chosen)
+    chunks = [{"l1": c[0], "q1": c[1], "l2": c[2], "budget_us": c[3], "chunk_blocks": p[3], "T_us": t[4]}
+              for c, p, t in zip(chunk_cases, chosen, timed)]
     res = {"model": "T = k1 + k2 (q1+q2) + k3 (l1+l2) + k4 q2 (l1+q1+l2+q2) + k5 q1 (l1+q1), sizes in 16-token blocks, T in us",
            "workload": f"{B} requests, GQA 32/8, d 128, bf16; step = msa_write_kv of the q1+q2 fresh blocks + msa_forward "
                        "of their query rows; median of 15 (grid) / 41 (checks) HIP-event timed steps",
            "k": model.k, "rms_rel": model.rms, "n": int(len(grid)), "dT_check_blocks_moved": D, "checks": rows,
+           "chunk_rule": chunks,
            "grid": grid.tolist(), "seconds": time.perf_counter() - t0}
     print(json.dumps({k: v for k, v in res.items() if k != "grid"}), flush=True)
     if args.latency_out:
@@ -340,6 +350,11 @@ def latency_report(src, dst, command):
     for r in res["checks"]:
         lines.append(f"| {r['l1']} | {r['q1']} | {r['l2']} | {r['q2']} | {r['T_us']:.1f} | {r['model_T_us']:.1f} | "
                      f"{r['measured_dT_us']:.1f} | {r['eq5_dT_us']:.1f} |")
+    if res.get("chunk_rule"):
+        lines += ["", "## Adaptive chunk size: largest chunk whose modelled step time fits the budget (512 blocks left)", "",
+                  "| l1 | q1 | l2 | budget (us) | chunk (blocks) | step time measured (us) |", "|---|---|---|---|---|---|"]
+        for r in res["chunk_rule"]:
+            lines.append(f"| {r['l1']} | {r['q1']} | {r['l2']} | {r['budget_us']:.0f} | {r['chunk_blocks']} | {r['T_us']:.1f} |")
     with open(dst, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {dst}")

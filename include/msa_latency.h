@@ -49,6 +49,17 @@ int msa_latency_eval(const msa_latency_model* model, double l1, double q1, doubl
 /* Eq. 5: dT_B at (l1, q1) of a fitted model. */
 int msa_latency_delta_b(const msa_latency_model* model, double l1, double q1, double* dt);
 
+/* Adaptive chunk size (the pages' adaptive chunking scheduler, abstract and
+ * summary: chunk sizes chosen for hardware utilisation).  For the next step of
+ * a request whose context holds l1 cached, q1 recomputed and l2 cached blocks
+ * and which still has `remaining` >= 1 new blocks to prefill: the largest c in
+ * [1, remaining] whose predicted step time T(l1, q1, l2, c) is <= budget (the
+ * step-time bound that keeps co-scheduled decode steps on time), so each step
+ * does as much work as the bound allows; 1 if even one block exceeds it.
+ * Errors: INVALID_ARG (NULL pointers, remaining < 1, non-finite arguments). */
+int msa_chunk_blocks(const msa_latency_model* model, double l1, double q1, double l2, int32_t remaining,
+                     double budget, int32_t* chunk);
+
 #ifdef __cplusplus
 }
 #endif

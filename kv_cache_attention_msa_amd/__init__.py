@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "MsaError", "Pool", "SegDesc", "forward", "write_kv", "plan_debug", "library_path", "load_library",
-    "LatencyModel", "latency_fit",
+    "LatencyModel", "latency_fit", "chunk_blocks",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
     "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS",
@@ -32,7 +32,7 @@ KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_
 EXPORTED_SYMBOLS = (
     "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_write_kv", "msa_last_error",
     "msa_pool_set_option", "msa_pool_kernel_time", "msa_plan_debug",
-    "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b",
+    "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b", "msa_chunk_blocks",
 )
 
 _ERR_NAMES = {ERR_INVALID_ARG: "INVALID_ARG", ERR_UNSUPPORTED: "UNSUPPORTED", ERR_OOM: "OOM",
@@ -101,6 +101,7 @@ def load_library():
     lib.msa_latency_fit.argtypes = [P, I32, I32, ctypes.POINTER(_LatencyModel)]
     lib.msa_latency_eval.argtypes = [ctypes.POINTER(_LatencyModel), D, D, D, D, ctypes.POINTER(D)]
     lib.msa_latency_delta_b.argtypes = [ctypes.POINTER(_LatencyModel), D, D, ctypes.POINTER(D)]
+    lib.msa_chunk_blocks.argtypes = [ctypes.POINTER(_LatencyModel), D, D, D, I32, D, ctypes.POINTER(I32)]
     for name in EXPORTED_SYMBOLS:
         if name != "msa_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -272,6 +273,14 @@ def latency_fit(samples, relative: bool = True) -> LatencyModel:
     m = _LatencyModel()
     _check(load_library().msa_latency_fit(s.ctypes.data, len(s), int(bool(relative)), ctypes.byref(m)))
     return LatencyModel(m)
+
+
+def chunk_blocks(model: LatencyModel, l1, q1, l2, remaining: int, budget: float) -> int:
+    """Blocks to prefill in the next step under a step-time budget (see msa_chunk_blocks)."""
+    c = ctypes.c_int32()
+    _check(load_library().msa_chunk_blocks(ctypes.byref(model.c), l1, q1, l2, int(remaining), budget,
+                                           ctypes.byref(c)))
+    return c.value
 
 
 def plan_debug(seg_desc: SegDesc, num_kv_heads: int, head_dim: int, dtype: int = BF16,

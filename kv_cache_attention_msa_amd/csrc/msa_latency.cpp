@@ -138,4 +138,26 @@ int msa_latency_delta_b(const msa_latency_model* model, double l1, double q1, do
   return MSA_OK;
 }
 
+int msa_chunk_blocks(const msa_latency_model* model, double l1, double q1, double l2, int32_t remaining,
+                     double budget, int32_t* chunk) {
+  if (!model || !chunk) return msa::set_error_msg(MSA_ERR_INVALID_ARG, "model or chunk is NULL");
+  if (remaining < 1) return msa::set_error_msg(MSA_ERR_INVALID_ARG, "remaining must be >= 1");
+  if (!finite_nonneg(l1) || !finite_nonneg(q1) || !finite_nonneg(l2) || std::isnan(budget))
+    return msa::set_error_msg(MSA_ERR_INVALID_ARG, "region sizes must be finite and >= 0, budget not NaN");
+  // Scan from the largest candidate down: no monotonicity of the fitted model
+  // is assumed (a fit may carry a negative coefficient).
+  double t[kTerms];
+  for (int32_t c = remaining; c >= 1; --c) {
+    terms(l1, q1, l2, (double)c, t);
+    double T = 0.0;
+    for (int j = 0; j < kTerms; ++j) T += model->k[j] * t[j];
+    if (T <= budget) {
+      *chunk = c;
+      return MSA_OK;
+    }
+  }
+  *chunk = 1;
+  return MSA_OK;
+}
+
 }  // extern "C"

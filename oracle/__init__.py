@@ -5,8 +5,8 @@ Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 may import this package.  It shares no code with the HIP path.
 """
 from .kv_write_oracle import write_kv
-from .latency_oracle import delta_b, fit_latency, latency, model_terms
+from .latency_oracle import chunk_blocks, delta_b, fit_latency, latency, model_terms
 from .msa_oracle import attend, gather_context, masked_softmax_attention, merge_partials
 
 __all__ = ["attend", "gather_context", "masked_softmax_attention", "merge_partials", "write_kv",
-           "delta_b", "fit_latency", "latency", "model_terms"]
+           "chunk_blocks", "delta_b", "fit_latency", "latency", "model_terms"]

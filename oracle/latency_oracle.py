@@ -24,9 +24,16 @@ measured times by least squares; with ``relative`` the residuals are taken
 relative to the measured time (rows scaled by 1/T), which suits timings whose
 noise grows with their size.
 
+Adaptive chunk size (the pages' adaptive chunking scheduler, named in the
+abstract for hardware utilisation; the rule itself is not given).  Reading
+taken: for the next step of a request with l1, q1, l2 blocks of context and
+``remaining`` new blocks, take the largest chunk c in [1, remaining] whose
+modelled step time T(l1, q1, l2, c) fits a per-step budget (1 if none does).
+
 Pins (``tests/test_latency_oracle.py``): the difference of T equals Eq. 5 as
 printed, exact recovery of known coefficients, exact interpolation through
-five points, and detection of a grid that cannot determine all five.
+five points, detection of a grid that cannot determine all five, and the
+chunk rule against the closed-form root of its quadratic.
 """
 from __future__ import annotations
 
@@ -66,3 +73,9 @@ def fit_latency(samples, relative=True):
     k, *_ = np.linalg.lstsq(Aw, tw, rcond=None)
     r = Aw @ k - tw
     return k, float(np.sqrt(np.mean(r * r)))
+
+
+def chunk_blocks(k, l1, q1, l2, remaining, budget):
+    """Largest c in [1, remaining] with T(l1, q1, l2, c) <= budget, else 1."""
+    fits = [c for c in range(1, int(remaining) + 1) if latency(k, l1, q1, l2, c) <= budget]
+    return max(fits) if fits else 1

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import kv_cache_attention_msa_amd as msa
-from oracle.latency_oracle import delta_b, fit_latency, latency
+from oracle.latency_oracle import chunk_blocks, delta_b, fit_latency, latency
 
 
 def _grid():
@@ -53,3 +53,27 @@ def test_bad_inputs():
     with pytest.raises(msa.MsaError):
         msa.latency_fit(bad, relative=True)                         # relative needs T > 0
     msa.latency_fit(bad, relative=False)                            # fine without
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_chunk_rule_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    k = np.array([30.0, 0.2, 0.19, 0.07, 0.07]) * rng.uniform(0.5, 2, size=5)
+    if seed == 3:
+        k[1] = -0.5                                   # a fit with a negative coefficient
+    g = _grid()
+    m = msa.latency_fit(np.column_stack([g, latency(k, *g.T)]))
+    for _ in range(20):
+        l1, q1, l2 = (float(x) for x in rng.integers(0, 300, size=3))
+        rem = int(rng.integers(1, 400))
+        budget = float(rng.uniform(10, 3000))
+        assert msa.chunk_blocks(m, l1, q1, l2, rem, budget) == chunk_blocks(m.k, l1, q1, l2, rem, budget)
+
+
+def test_chunk_rule_bad_inputs():
+    g = _grid()
+    m = msa.latency_fit(np.column_stack([g, latency([1, 1, 1, 1, 1], *g.T)]))
+    with pytest.raises(msa.MsaError):
+        msa.chunk_blocks(m, 0, 0, 0, 0, 100.0)
+    with pytest.raises(msa.MsaError):
+        msa.chunk_blocks(m, -1, 0, 0, 5, 100.0)

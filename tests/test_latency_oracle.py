@@ -10,7 +10,7 @@ import itertools
 import numpy as np
 import pytest
 
-from oracle.latency_oracle import delta_b, fit_latency, latency, model_terms
+from oracle.latency_oracle import chunk_blocks, delta_b, fit_latency, latency, model_terms
 
 
 def eq5_as_printed(k, l1, q1):
@@ -75,3 +75,18 @@ def test_undetermined_grid_rejected():
         fit_latency(np.column_stack([g, T]))
     with pytest.raises(ValueError):
         fit_latency(np.zeros((4, 5)) + 1)
+
+
+def test_chunk_rule_is_the_root_of_its_quadratic():
+    # T(l1, q1, l2, c) = k1 + k2 (q1 + c) + k3 (l1 + l2) + k4 c (l1 + q1 + l2 + c) + k5 q1 (l1 + q1)
+    # is k4 c^2 + b c + a; the rule must return floor of the larger root of T = budget.
+    k = [30.0, 0.2, 0.19, 0.07, 0.07]
+    l1, q1, l2, budget = 100, 10, 50, 900.0
+    a = k[0] + k[1] * q1 + k[2] * (l1 + l2) + k[4] * q1 * (l1 + q1) - budget
+    b = k[1] + k[3] * (l1 + q1 + l2)
+    root = (-b + np.sqrt(b * b - 4 * k[3] * a)) / (2 * k[3])
+    assert chunk_blocks(k, l1, q1, l2, 10_000, budget) == int(np.floor(root))
+    assert chunk_blocks(k, l1, q1, l2, 5, budget) == 5                 # capped by what is left
+    assert chunk_blocks(k, l1, q1, l2, 10_000, 1.0) == 1               # nothing fits: still progress
+    sizes = [chunk_blocks(k, l1, q1, l2, 10_000, t) for t in (200, 400, 800, 1600)]
+    assert sizes == sorted(sizes)                                      # a larger budget never shrinks it
