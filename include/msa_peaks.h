@@ -18,7 +18,7 @@ extern "C" {
 #endif
 
 /* Streaming read of `bytes` (multiple of 16, > 0) of device memory, 16 bytes
- * per lane per load, `iters` timed passes; *gbps = bytes * iters / time. */
+ * per lane per non-temporal load, `iters` timed passes; *gbps = bytes * iters / time. */
 int msa_peak_hbm_read(size_t bytes, int iters, double* gbps);
 
 /* Device-to-device copy of `bytes` (multiple of 16, > 0), 16 bytes per lane,

@@ -18,7 +18,8 @@
 //   * keys outside a block's valid slots, past the item's blocks, or (causal)
 //     at a position after the row's query position get score -inf by select;
 //     steps that are entirely visible to every row skip the mask;
-//   * online softmax in the exp2 domain (scale * log2 e folded into one FMA);
+//   * online softmax in the exp2 domain (scale * log2 e folded into one FMA)
+//     against a per-row reference that moves only when needed;
 //   * P is rounded to bf16 in place of the S accumulator registers and used as
 //     the B operand of O^T += V^T P^T.
 // Slots that hold no key are zero-filled in LDS, so the 0-probabilities never
@@ -35,6 +36,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
+constexpr float kRefSumLimit = 1048576.f;  // 2^20: largest accepted partial row sum per step
 
 // LDS tiles.  gfx950's LDS serves a ds_read_b128 16 lanes per clock (64 banks
 // x 4 bytes), so an operand read is conflict-free when the 16 lanes of each
@@ -215,27 +217,38 @@ __device__ __forceinline__ void mask_half(f32x16& s0, f32x16& s1, const StepMeta
 }
 
 __device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1) {
-  float mx = kNegInf;
+  float m0 = kNegInf, m1 = kNegInf;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s0[r], s1[r]));
+  for (int r = 0; r < 16; r += 2) {
+    m0 = __builtin_fmaxf(m0, __builtin_fmaxf(s0[r], s0[r + 1]));
+    m1 = __builtin_fmaxf(m1, __builtin_fmaxf(s1[r], s1[r + 1]));
+  }
+  const float mx = fmaxf(m0, m1);
   return fmaxf(mx, __shfl_xor(mx, 32, 64));
 }
 
-// p = exp2(s * c2 - m) rounded to bf16 in pw (word j of kb: regs 2j, 2j+1);
-// returns this lane's part of the row sum (the other lane half holds the rest).
-__device__ __forceinline__ float exp_half(const f32x16& s0, const f32x16& s1, float c2, float m_use, uint32_t (&pw)[16]) {
-  float rs = 0.f;
+// p = exp2(s * c2 - mu) rounded to bf16 in pw (word j of kb: regs 2j, 2j+1);
+// returns this lane's part of the row sum (the other lane half holds the
+// rest), summed from the rounded p that the PV product uses, two at a time
+// (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float exp_half(const f32x16& s0, const f32x16& s1, float c2, float mu, uint32_t (&pw)[16]) {
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -m_use));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, -m_use));
-    const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -m_use));
-    const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, -m_use));
-    rs += (p0 + p1) + (p2 + p3);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -mu));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, -mu));
+    const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -mu));
+    const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, -mu));
     pw[r / 2] = pack_bf16x2(p0, p1);
     pw[8 + r / 2] = pack_bf16x2(p2, p3);
   }
-  return rs;
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float ra = 0.f, rb = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    ra = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]), one, ra, false);
+    rb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j + 1]), one, rb, false);
+  }
+  return ra + rb;
 }
 
 struct RowInfo {
@@ -335,25 +348,6 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
 
       // ---- S^T = K Q^T for 64 keys ----
       f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
-#ifdef MSA_SETPRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-#ifdef MSA_PIPE_OPS
-      bf16x8 k0 = ld_k<D>(sm, buf, col, h), k1 = ld_k<D>(sm, buf, 32 + col, h);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 n0 = k0, n1 = k1;
-        if (ks + 1 < D / 16) {
-          n0 = ld_k<D>(sm, buf, col, 2 * (ks + 1) + h);
-          n1 = ld_k<D>(sm, buf, 32 + col, 2 * (ks + 1) + h);
-        }
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
-        k0 = n0;
-        k1 = n1;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#else
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 k0 = ld_k<D>(sm, buf, col, 2 * ks + h);
@@ -361,53 +355,35 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
       }
-#endif
-#ifdef MSA_SETPRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
       stage_k<D>(sm, buf ^ 1, regs, t);
       fetch_v<D>(a, it.kv_head, nxt, regs, t);
 
       if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
 
       // ---- online softmax (exp2 domain) ----
-      // The reference max of a row only moves when the row max exceeds it by
-      // more than 2^8: exact (output and row sum share the reference), p stays
-      // <= 256, and most steps skip rescaling the accumulators.
-      const float mx = row_max(s0, s1) * c2;
-      const bool grow = mx > m + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        // rows that keep their reference get alpha = 1 (also when it is -inf)
+      // Probabilities are taken against a per-row reference m instead of the
+      // exact running max: exact all the same, since output and row sum share
+      // the reference.  The reference only has to keep exp2 in range, so the
+      // row max is computed only when a lane's partial row sum leaves
+      // [0, 2^20] (some p > 2^15) or the row has no reference yet; then rows
+      // whose max exceeds m by more than 2^8 move m to it, rescale their
+      // accumulators and recompute p.  In steady state a step costs no max
+      // and no rescale.
+      uint32_t pw[16];
+      float rs = exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
+      if (__builtin_amdgcn_ballot_w64(m == kNegInf || !(rs <= kRefSumLimit))) {
+        const float mx = row_max(s0, s1) * c2;
+        const bool grow = mx != kNegInf && (m == kNegInf || mx > m + 8.f);
         const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;  // m = -inf: 0
         m = grow ? mx : m;
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        rs = exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
       }
-      uint32_t pw[16];
-      l += exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
+      l += rs;
 
       // ---- O^T += V^T P^T ----
-#ifdef MSA_SETPRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-#ifdef MSA_PIPE_OPS
-      bf16x8 v = ld_vt<D>(sm, buf, col, h);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
-        const bf16x8 pop = as_bf16x8(make_uint4(pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]));
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int nks = (db + 1 < D / 32) ? ks : ks + 1, ndb = (db + 1 < D / 32) ? db + 1 : 0;
-          bf16x8 nv = v;
-          if (nks < 4) nv = ld_vt<D>(sm, buf, ndb * 32 + col, 2 * nks + h);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
-          v = nv;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#else
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
@@ -418,10 +394,6 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
         }
       }
-#endif
-#ifdef MSA_SETPRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
 
       stage_v<D>(sm, buf ^ 1, regs, nxt, t);
       cur = nxt;

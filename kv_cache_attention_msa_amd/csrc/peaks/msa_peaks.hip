@@ -9,11 +9,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, size_t n, uint32_t* out) {
   uint32_t acc = 0;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(p + i));
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads live; practically never taken
 }

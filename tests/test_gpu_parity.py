@@ -88,6 +88,21 @@ def test_edge_cases():
         _check(wl, split_blocks=2)
 
 
+@pytest.mark.parametrize("factor", [30.0, 300.0])
+def test_reference_moves_mid_row(factor):
+    """Scores that jump by far more than 2^20 (log2 domain) partway through a
+    row: the kernel's per-row reference must move and rescale mid-row, both
+    within a step and across KV splits."""
+    wl = W.custom([([(0, 300), (300, 100), (400, 200, W.SEG_FRESH)], list(range(400, 600)))],
+                  H_q=8, H_kv=2, d=128, seed=12)
+    first, second = -(-300 // 16), -(-100 // 16)          # blocks of the first two segments, in build order
+    k = wl.k_blocks.float()
+    k[first:first + second] *= factor                     # the middle segment's keys dominate
+    wl.k_blocks = k.to(torch.bfloat16)
+    _check(wl)
+    _check(wl, split_blocks=3)
+
+
 def test_empty_batch_and_no_queries():
     wl = W.custom([([(0, 40)], [])], H_q=4, H_kv=1, d=128)
     case = GpuCase(wl)
