@@ -82,7 +82,20 @@ def traffic_for(kernel, units):
     return rec.get("bytes_per_launch")
 
 
-def run_workload(wl, steps, warmup, kind):
+def percentiles(samples_ms):
+    """p10 / median / p90 of per-launch durations (ms)."""
+    import numpy as np
+    if len(samples_ms) == 0:
+        return None
+    p10, p50, p90 = np.percentile(np.asarray(samples_ms), [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "n": int(len(samples_ms))}
+
+
+def run_workload(wl, steps, warmup, kind, cold=False):
+    """Time msa_forward over the workload: wall clock per call over back-to-back
+    calls, then per-kernel HIP-event times (totals and per-launch samples for
+    `kind`); with cold, also `kind`'s launch times when a 1 GiB read between
+    calls has evicted the Infinity Cache."""
     import torch
     import kv_cache_attention_msa_amd as msa
 
@@ -109,6 +122,16 @@ def run_workload(wl, steps, warmup, kind):
         msa.forward(q, desc, bt, pool, out, lse, stream)
     torch.cuda.synchronize()
     times = {k: pool.kernel_time(k) for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE, msa.KERNEL_MERGE)}
+    times["dist"] = percentiles(pool.kernel_samples(kind))
+    if cold:
+        flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+        pool.kernel_time(kind, reset=True)
+        for _ in range(steps):
+            flush.sum()
+            msa.forward(q, desc, bt, pool, out, lse, stream)
+        torch.cuda.synchronize()
+        times["cold_dist"] = percentiles(pool.kernel_samples(kind))
+        del flush
     # host planning + packing cost of one call (no device work): time the
     # planner alone through its host-only export
     t1 = time.perf_counter()
@@ -151,15 +174,18 @@ def run_write(wl, fresh, steps, warmup):
     for _ in range(steps):
         msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
     torch.cuda.synchronize()
+    warm_dist = percentiles(pool.kernel_samples(msa.KERNEL_WRITE))
     warm_ms, warm_n = pool.kernel_time(msa.KERNEL_WRITE, reset=True)
     for _ in range(steps):
         flush.sum()
         msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
     torch.cuda.synchronize()
     cold_ms, cold_n = pool.kernel_time(msa.KERNEL_WRITE)
+    cold_dist = percentiles(pool.kernel_samples(msa.KERNEL_WRITE))
     pool.close()
     del K, V, flush
     torch.cuda.empty_cache()
+    run_write.dists = {"warm": warm_dist, "cold": cold_dist}
     return wall / steps * 1e3, warm_ms / max(warm_n, 1), cold_ms / max(cold_n, 1), cold_n
 
 
@@ -444,7 +470,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
                 "traffic": traffic_for("prefill", wl.name),
-                "kernel": "msa_prefill (bf16 MFMA)", "kernel_ms": k_avg,
+                "kernel": "msa_prefill (bf16 MFMA)", "kernel_ms": k_avg, "kernel_ms_dist": times["dist"],
                 "merge_ms": mrg_ms / mrg_n if mrg_n else 0.0, "launches_per_step": (pre_n + dec_n + mrg_n) / args.steps}
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -459,7 +485,7 @@ def main():
     if not args.no_secondary:
         wl3 = W.config3()
         f3, b3 = work_of(wl3)
-        ms3, t3, plan3 = run_workload(wl3, args.steps, args.warmup, msa.KERNEL_DECODE)
+        ms3, t3, plan3 = run_workload(wl3, args.steps, args.warmup, msa.KERNEL_DECODE, cold=True)
         d_ms, d_n = t3[msa.KERNEL_DECODE]
         m_ms, m_n = t3[msa.KERNEL_MERGE]
         d_avg = d_ms / max(d_n, 1)
@@ -470,7 +496,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": ach / PEAK_HBM_GBS if ach else None,
                          "traffic": traffic_for("decode", wl3.name), "kernel": "msa_decode",
-                         "kernel_ms": d_avg, "merge_ms": m_ms / m_n if m_n else 0.0},
+                         "kernel_ms": d_avg, "kernel_ms_dist": t3["dist"],
+                         "kernel_ms_dist_cold": t3["cold_dist"], "merge_ms": m_ms / m_n if m_n else 0.0},
         }
         del wl3
         wl5 = W.config5()
@@ -486,7 +513,9 @@ def main():
                          "frac": ach5 / PEAK_HBM_GBS if ach5 else None,
                          "traffic": traffic_for("write", wl5.name + "_fresh"), "kernel": "msa_write",
                          "kernel_ms": k5, "cache": "cold (1 GiB read between calls evicts the Infinity Cache)",
-                         "kernel_warm_ms": k5w, "achieved_warm": b5 / (k5w * 1e-3) / 1e9 if n5 else None},
+                         "kernel_warm_ms": k5w, "achieved_warm": b5 / (k5w * 1e-3) / 1e9 if n5 else None,
+                         "kernel_ms_dist_cold": run_write.dists["cold"],
+                         "kernel_ms_dist_warm": run_write.dists["warm"]},
         }
         del wl5, fresh
     att = attainable_peaks()

@@ -192,6 +192,13 @@ int msa_pool_set_option(msa_pool* pool, int32_t option, int64_t value);
 int msa_pool_kernel_time(msa_pool* pool, int32_t kind, double* total_ms, int64_t* launches,
                          int32_t reset);
 
+/* With MSA_OPT_TIMING on: the durations (ms) of the most recent launches of
+ * `kind` since the last reset, oldest first, at most `max` of them, written
+ * to out (host array); *n receives the count.  The pool keeps up to 65 536
+ * durations per kind (older ones are dropped).  Synchronises like
+ * msa_pool_kernel_time.  Errors: INVALID_ARG, HIP. */
+int msa_pool_kernel_samples(msa_pool* pool, int32_t kind, double* out, int32_t max, int32_t* n);
+
 /* One work item of a plan (as the kernels see it). */
 typedef struct {
   int32_t kind;       /* MSA_KERNEL_PREFILL / DECODE / FP32                       */

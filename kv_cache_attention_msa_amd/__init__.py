@@ -31,7 +31,7 @@ KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_
 
 EXPORTED_SYMBOLS = (
     "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_write_kv", "msa_last_error",
-    "msa_pool_set_option", "msa_pool_kernel_time", "msa_plan_debug",
+    "msa_pool_set_option", "msa_pool_kernel_time", "msa_pool_kernel_samples", "msa_plan_debug",
     "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b", "msa_chunk_blocks",
 )
 
@@ -95,6 +95,7 @@ def load_library():
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_pool_set_option.argtypes = [P, I32, I64]
     lib.msa_pool_kernel_time.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
+    lib.msa_pool_kernel_samples.argtypes = [P, I32, P, I32, ctypes.POINTER(I32)]
     lib.msa_plan_debug.argtypes = [ctypes.POINTER(_SegDesc), I32, I32, I32, I32, I32, P, I32,
                                    ctypes.POINTER(I32), P, I32, ctypes.POINTER(I32)]
     D = ctypes.c_double
@@ -189,6 +190,14 @@ class Pool:
         ms, n = ctypes.c_double(), ctypes.c_int64()
         _check(load_library().msa_pool_kernel_time(self.handle, kind, ctypes.byref(ms), ctypes.byref(n), int(reset)))
         return ms.value, n.value
+
+    def kernel_samples(self, kind: int, max_samples: int = 1 << 16):
+        """Per-launch durations (ms) of `kind` since the last reset, oldest first."""
+        out = np.zeros(max_samples, dtype=np.float64)
+        n = ctypes.c_int32()
+        _check(load_library().msa_pool_kernel_samples(self.handle, kind, out.ctypes.data, max_samples,
+                                                      ctypes.byref(n)))
+        return out[:n.value]
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

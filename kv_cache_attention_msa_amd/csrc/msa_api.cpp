@@ -115,6 +115,8 @@ struct msa_pool {
   std::vector<hipEvent_t> spare_events;
   double total_ms[kNumKinds] = {};
   int64_t launches[kNumKinds] = {};
+  static constexpr size_t kMaxSamples = 1 << 16;  // per kind; the oldest are dropped beyond this
+  std::vector<float> samples[kNumKinds];
 
   Plan plan;
   std::vector<BlockEntry> write_entries;  // msa_write_kv's block list
@@ -139,6 +141,9 @@ int collect_timing(msa_pool* p) {
     MSA_HIP(hipEventElapsedTime(&ms, r.start, r.stop));
     p->total_ms[r.kind] += ms;
     p->launches[r.kind] += 1;
+    std::vector<float>& v = p->samples[r.kind];
+    if (v.size() >= msa_pool::kMaxSamples) v.erase(v.begin(), v.begin() + v.size() / 2);
+    v.push_back(ms);
     p->spare_events.push_back(r.start);
     p->spare_events.push_back(r.stop);
   }
@@ -366,8 +371,25 @@ int msa_pool_kernel_time(msa_pool* p, int32_t kind, double* total_ms, int64_t* l
     for (int k = 0; k < kNumKinds; ++k) {
       p->total_ms[k] = 0;
       p->launches[k] = 0;
+      p->samples[k].clear();
     }
   }
+  return MSA_OK;
+}
+
+int msa_pool_kernel_samples(msa_pool* p, int32_t kind, double* out, int32_t max, int32_t* n) {
+  if (!p || !n || (max > 0 && !out)) return set_error(MSA_ERR_INVALID_ARG, "NULL argument");
+  if (kind < 0 || kind >= kNumKinds) return set_error(MSA_ERR_INVALID_ARG, "bad kernel kind %d", kind);
+  if (max < 0) return set_error(MSA_ERR_INVALID_ARG, "max < 0");
+  if (!p->records.empty()) {
+    DeviceGuard g(p->desc.device);
+    int rc = collect_timing(p);
+    if (rc) return rc;
+  }
+  const std::vector<float>& v = p->samples[kind];
+  const size_t k = std::min(v.size(), (size_t)max);
+  for (size_t i = 0; i < k; ++i) out[i] = v[v.size() - k + i];
+  *n = (int32_t)k;
   return MSA_OK;
 }
 
