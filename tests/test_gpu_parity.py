@@ -103,6 +103,31 @@ def test_reference_moves_mid_row(factor):
     _check(wl, split_blocks=3)
 
 
+def test_timing_records_every_launch():
+    """With timing on, every launch of a kind is recorded once, with a positive duration."""
+    wl = W.random_case(70, batch=3, H_q=8, H_kv=2, d=128, max_ctx=600, max_chunk=80)
+    case = GpuCase(wl)
+    try:
+        case.pool.set_option(msa.OPT_TIMING, 1)
+        case.pool.set_option(msa.OPT_SPLIT_BLOCKS, 3)     # forces split items and the merge kernel
+        for k in range(5):
+            case.pool.kernel_time(k, reset=True)
+        for _ in range(3):
+            msa.forward(case.q, case.desc, case.bt, case.pool, case.out, case.lse)
+        torch.cuda.synchronize()
+        for kind in (msa.KERNEL_UPLOAD, msa.KERNEL_MERGE):
+            total, n = case.pool.kernel_time(kind)
+            samples = case.pool.kernel_samples(kind)
+            assert n == 3 and len(samples) == 3, (kind, n, len(samples))
+            assert (samples > 0).all() and abs(samples.sum() - total) < 1e-3 * max(total, 1e-3)
+        launched = sum(case.pool.kernel_time(k)[1] for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE))
+        assert launched >= 3
+        case.pool.kernel_time(msa.KERNEL_UPLOAD, reset=True)
+        assert len(case.pool.kernel_samples(msa.KERNEL_UPLOAD)) == 0
+    finally:
+        case.close()
+
+
 def test_empty_batch_and_no_queries():
     wl = W.custom([([(0, 40)], [])], H_q=4, H_kv=1, d=128)
     case = GpuCase(wl)

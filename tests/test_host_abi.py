@@ -305,3 +305,24 @@ def test_write_kv_argument_checks():
         assert "block-table entry 1" in lib.msa_last_error().decode()
     finally:
         lib.msa_destroy_pool(h)
+
+
+def test_kernel_time_and_samples_argument_checks():
+    h = _fake_pool()
+    lib = msa.load_library()
+    try:
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        assert lib.msa_pool_kernel_time(h, 99, ctypes.byref(ms), ctypes.byref(n), 0) == msa.ERR_INVALID_ARG
+        assert lib.msa_pool_kernel_time(h, msa.KERNEL_PREFILL, ctypes.byref(ms), ctypes.byref(n), 0) == msa.OK
+        assert ms.value == 0.0 and n.value == 0
+        out = np.zeros(4)
+        cnt = ctypes.c_int32(-1)
+        assert lib.msa_pool_kernel_samples(h, msa.KERNEL_DECODE, out.ctypes.data, 4, ctypes.byref(cnt)) == msa.OK
+        assert cnt.value == 0
+        assert lib.msa_pool_kernel_samples(h, -1, out.ctypes.data, 4, ctypes.byref(cnt)) == msa.ERR_INVALID_ARG
+        assert lib.msa_pool_kernel_samples(h, 0, None, 4, ctypes.byref(cnt)) == msa.ERR_INVALID_ARG
+        assert lib.msa_pool_kernel_samples(h, 0, out.ctypes.data, -1, ctypes.byref(cnt)) == msa.ERR_INVALID_ARG
+        assert lib.msa_pool_kernel_samples(h, 0, out.ctypes.data, 4, None) == msa.ERR_INVALID_ARG
+        assert lib.msa_pool_set_option(h, 77, 1) == msa.ERR_INVALID_ARG
+    finally:
+        lib.msa_destroy_pool(h)
