@@ -205,14 +205,17 @@ def attainable_peaks():
     lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_attention_msa_amd", "libmsa_peaks.so"))
     lib.msa_peak_hbm_read.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.msa_peak_hbm_copy.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.msa_peak_hbm_gather.argtypes = [ctypes.c_int32, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.msa_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
-    gbps, copy, tflops = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    gbps, copy, gather, tflops = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     assert lib.msa_peak_hbm_read(4 << 30, 5, ctypes.byref(gbps)) == 0
     assert lib.msa_peak_hbm_copy(1 << 30, 5, ctypes.byref(copy)) == 0
+    assert lib.msa_peak_hbm_gather(1 << 18, 5, ctypes.byref(gather)) == 0
     assert lib.msa_peak_mfma_bf16(4000, ctypes.byref(tflops)) == 0
-    return {"hbm_read_GBps": gbps.value, "hbm_copy_GBps": copy.value, "mfma_bf16_TFLOPs": tflops.value,
-            "how": "libmsa_peaks.so: streaming 4 GiB read; 1 GiB device copy (read + write bytes); "
-                   "v_mfma_f32_32x32x16_bf16 loop on independent accumulators"}
+    return {"hbm_read_GBps": gbps.value, "hbm_gather_4KiB_GBps": gather.value, "hbm_copy_GBps": copy.value,
+            "mfma_bf16_TFLOPs": tflops.value,
+            "how": "libmsa_peaks.so: streaming 4 GiB read; 1 GiB of scattered 4 KiB blocks (of a 2 GiB buffer); "
+                   "1 GiB device copy (read + write bytes); v_mfma_f32_32x32x16_bf16 loop on independent accumulators"}
 
 
 def cpu_baseline(wl, flops_per_row, budget_s=12.0):
@@ -521,7 +524,7 @@ def main():
     att = attainable_peaks()
     line["attainable"] = att
     roofline["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOPs"] if achieved else None
-    for key, ref in (("secondary", "hbm_read_GBps"), ("kv_write", "hbm_copy_GBps")):
+    for key, ref in (("secondary", "hbm_gather_4KiB_GBps"), ("kv_write", "hbm_copy_GBps")):
         if key in line:
             sr = line[key]["roofline"]
             sr["frac_of_attainable"] = sr["achieved"] / att[ref] if sr["achieved"] else None

@@ -12,6 +12,7 @@
 #define MSA_PEAKS_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -25,6 +26,12 @@ int msa_peak_hbm_read(size_t bytes, int iters, double* gbps);
  * non-temporal stores, `iters` timed passes; *gbps counts each byte once read and once written:
  * 2 * bytes * iters / time. */
 int msa_peak_hbm_copy(size_t bytes, int iters, double* gbps);
+
+/* Gather of `blocks` 4 KiB blocks at scattered places of a buffer of
+ * 2 * blocks * 4 KiB (a seeded permutation, fixed per call), 16 bytes per lane
+ * per non-temporal load, one wave per block, `iters` timed passes; *gbps =
+ * blocks * 4 KiB * iters / time.  The access pattern of a block-paged KV pool. */
+int msa_peak_hbm_gather(int32_t blocks, int iters, double* gbps);
 
 /* v_mfma_f32_32x32x16_bf16 issued back to back on independent accumulators by
  * every wave of a full-device grid, operands in registers, `iters` loop trips;

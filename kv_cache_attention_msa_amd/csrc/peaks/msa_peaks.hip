@@ -2,6 +2,9 @@
 // a bf16 MFMA issue loop.  Measurement tooling for the benchmark only.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+#include <vector>
+
 #include "msa_peaks.h"
 
 namespace {
@@ -15,6 +18,22 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, 
   uint32_t acc = 0;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(p + i));
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads live; practically never taken
+}
+
+// One wave per 4 KiB block: 4 loads of 16 bytes per lane.
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ pool, const int32_t* __restrict__ ids,
+                                                     int32_t blocks, uint32_t* out) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= blocks) return;
+  const int lane = threadIdx.x & 63;
+  const u32x4_t* b = (const u32x4_t*)(pool + (size_t)ids[w] * 256);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t v = __builtin_nontemporal_load(b + j * 64 + lane);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads live; practically never taken
@@ -116,6 +135,50 @@ extern "C" int msa_peak_hbm_copy(size_t bytes, int iters, double* gbps) {
   if (s) (void)hipStreamDestroy(s);
   if (dst) (void)hipFree(dst);
   if (src) (void)hipFree(src);
+  return rc;
+}
+
+extern "C" int msa_peak_hbm_gather(int32_t blocks, int iters, double* gbps) {
+  if (!gbps || blocks <= 0 || iters <= 0) return -1;
+  const size_t pool_blocks = 2 * (size_t)blocks;
+  std::vector<int32_t> ids(pool_blocks);
+  for (size_t i = 0; i < pool_blocks; ++i) ids[i] = (int32_t)i;
+  uint64_t x = 0x2545F4914F6CDD1Dull;  // xorshift64*, fixed seed
+  for (size_t i = pool_blocks - 1; i > 0; --i) {
+    x ^= x >> 12; x ^= x << 25; x ^= x >> 27;
+    const size_t j = (size_t)((x * 0x2545F4914F6CDD1Dull) % (i + 1));
+    std::swap(ids[i], ids[j]);
+  }
+  void* pool = nullptr;
+  int32_t* d_ids = nullptr;
+  uint32_t* out = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = -5;
+  const size_t bytes = pool_blocks * 4096;
+  if (hipMalloc(&pool, bytes) == hipSuccess && hipMalloc(&d_ids, blocks * sizeof(int32_t)) == hipSuccess &&
+      hipMalloc(&out, 64) == hipSuccess && hipMemset(pool, 1, bytes) == hipSuccess &&
+      hipMemcpy(d_ids, ids.data(), blocks * sizeof(int32_t), hipMemcpyHostToDevice) == hipSuccess &&
+      hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess && hipEventCreate(&e0) == hipSuccess &&
+      hipEventCreate(&e1) == hipSuccess) {
+    const dim3 grid((unsigned)((blocks + 3) / 4));
+    hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, (const uint4*)pool, d_ids, blocks, out);
+    (void)hipEventRecord(e0, s);
+    for (int i = 0; i < iters; ++i)
+      hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, (const uint4*)pool, d_ids, blocks, out);
+    (void)hipEventRecord(e1, s);
+    float ms = 0.f;
+    if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.f) {
+      *gbps = (double)blocks * 4096.0 * iters / (ms * 1e-3) / 1e9;
+      rc = 0;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (s) (void)hipStreamDestroy(s);
+  if (out) (void)hipFree(out);
+  if (d_ids) (void)hipFree(d_ids);
+  if (pool) (void)hipFree(pool);
   return rc;
 }
 

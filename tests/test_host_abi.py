@@ -31,7 +31,7 @@ def test_peaks_library_exports_its_header():
     lib = ct.CDLL(path)
     text = open(os.path.join(os.path.dirname(HEADER), "msa_peaks.h")).read()
     declared = set(re.findall(r"^int\s+(msa_\w+)\s*\(", text, flags=re.M))
-    assert declared == {"msa_peak_hbm_read", "msa_peak_hbm_copy", "msa_peak_mfma_bf16"}
+    assert declared == {"msa_peak_hbm_read", "msa_peak_hbm_copy", "msa_peak_hbm_gather", "msa_peak_mfma_bf16"}
     for name in declared:
         assert hasattr(lib, name), name
 
