@@ -35,7 +35,7 @@ static int fail(std::string& err, int code, const char* fmt, ...) {
 namespace {
 
 struct Tile {
-  int32_t kind, seq, q_min, q_row0, n_q, blk_begin, blk_end;
+  int32_t kind, seq, q_min, q_row0, n_q, blk_begin, blk_end, nsplit;
 };
 
 // Largest block-count of one work item before the planner splits a tile.
@@ -47,11 +47,44 @@ int64_t auto_chunk(int kind, int64_t total_blocks, int num_cus) {
   return std::max<int64_t>(min_chunk, (total_blocks + slots - 1) / slots);
 }
 
+// Working lists of the planner, kept per thread so that a call allocates
+// nothing once they have grown.
+std::vector<Tile>& plan_tiles() {
+  thread_local std::vector<Tile> v;
+  return v;
+}
+std::vector<int32_t>& plan_order() {
+  thread_local std::vector<int32_t> v;
+  return v;
+}
+
+// Stable sort of work items by block count, largest first.  Block counts
+// are bounded by the split chunk, so a counting sort is the usual path.
+void sort_by_size(std::vector<WorkItem>& v) {
+  const size_t n = v.size();
+  if (n < 2) return;
+  int32_t mx = 0;
+  for (const WorkItem& w : v) mx = std::max(mx, w.blk_end - w.blk_begin);
+  if ((size_t)mx > 4 * n + 4096) {
+    std::stable_sort(v.begin(), v.end(), [](const WorkItem& x, const WorkItem& y) {
+      return (x.blk_end - x.blk_begin) > (y.blk_end - y.blk_begin);
+    });
+    return;
+  }
+  thread_local std::vector<int32_t> start;
+  thread_local std::vector<WorkItem> tmp;
+  start.assign((size_t)mx + 2, 0);
+  for (const WorkItem& w : v) ++start[(size_t)(mx - (w.blk_end - w.blk_begin)) + 1];
+  for (size_t i = 1; i < start.size(); ++i) start[i] += start[i - 1];
+  tmp.resize(n);
+  for (const WorkItem& w : v) tmp[(size_t)start[(size_t)(mx - (w.blk_end - w.blk_begin))]++] = w;
+  v.swap(tmp);
+}
+
 }  // namespace
 
 int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::string& err) {
   const int INV = MSA_ERR_INVALID_ARG, UNS = MSA_ERR_UNSUPPORTED;
-  plan.blocks.clear();
   plan.q_pos.clear();
   for (auto& v : plan.items) v.clear();
   plan.merges.clear();
@@ -80,7 +113,10 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
     return fail(err, MSA_ERR_WORKSPACE, "block_table_len %d exceeds 2^%d", d->block_table_len,
                 kBtIndexBits);
   const int B = d->batch;
-  if (B == 0) return MSA_OK;
+  if (B == 0) {
+    plan.blocks.clear();
+    return MSA_OK;
+  }
   if (!d->q_offsets || !d->seg_offsets) return fail(err, INV, "q_offsets or seg_offsets is NULL");
   if (d->q_offsets[0] != 0 || d->seg_offsets[0] != 0)
     return fail(err, INV, "q_offsets[0] and seg_offsets[0] must be 0");
@@ -98,45 +134,67 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   if (total_segs > 0 && !d->segs) return fail(err, INV, "segs is NULL");
   plan.total_q = total_q;
 
-  std::vector<Tile> tiles;
-  std::vector<int32_t> order;
+  // Segments: checks, and the number of blocks they cover in all.
+  int64_t n_blocks = 0;
+  for (int32_t s = 0; s < total_segs; ++s) {
+    const msa_segment& sg = d->segs[s];
+    if (sg.len < 0 || sg.pos_start < 0 || sg.bt_start < 0)
+      return fail(err, INV, "segment %d: negative pos_start, len or bt_start", s);
+    if ((int64_t)sg.pos_start + sg.len > std::numeric_limits<int32_t>::max())
+      return fail(err, INV, "segment %d: pos_start + len overflows int32", s);
+    const int64_t nblk = (sg.len + kBlock - 1) / kBlock;
+    if ((int64_t)sg.bt_start + nblk > d->block_table_len)
+      return fail(err, INV, "segment %d: blocks [%d, %lld) exceed block_table_len %d", s, sg.bt_start,
+                  (long long)(sg.bt_start + nblk), d->block_table_len);
+    n_blocks += nblk;
+  }
+  if (n_blocks > std::numeric_limits<int32_t>::max() / 2)
+    return fail(err, MSA_ERR_WORKSPACE, "%lld blocks in one call exceed 2^30", (long long)n_blocks);
+  // resize() keeps the entries of an earlier call; every one is rewritten below
+  plan.blocks.resize((size_t)n_blocks);
+
+  std::vector<Tile>& tiles = plan_tiles();
+  std::vector<int32_t>& order = plan_order();
+  tiles.clear();
+  int32_t cursor = 0;
   for (int b = 0; b < B; ++b) {
     const int32_t s0 = d->seg_offsets[b], s1 = d->seg_offsets[b + 1];
+    // Segments in position order; callers usually pass them so already.
+    bool sorted = true;
+    for (int32_t s = s0 + 1; s < s1 && sorted; ++s) sorted = d->segs[s - 1].pos_start <= d->segs[s].pos_start;
     order.clear();
-    for (int32_t s = s0; s < s1; ++s) {
-      const msa_segment& sg = d->segs[s];
-      if (sg.len < 0 || sg.pos_start < 0 || sg.bt_start < 0)
-        return fail(err, INV, "segment %d: negative pos_start, len or bt_start", s);
-      if ((int64_t)sg.pos_start + sg.len > std::numeric_limits<int32_t>::max())
-        return fail(err, INV, "segment %d: pos_start + len overflows int32", s);
-      const int64_t nblk = (sg.len + kBlock - 1) / kBlock;
-      if ((int64_t)sg.bt_start + nblk > d->block_table_len)
-        return fail(err, INV, "segment %d: blocks [%d, %lld) exceed block_table_len %d", s,
-                    sg.bt_start, (long long)(sg.bt_start + nblk), d->block_table_len);
-      if (sg.len > 0) order.push_back(s);
-    }
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-      return d->segs[x].pos_start < d->segs[y].pos_start;
-    });
+    for (int32_t s = s0; s < s1; ++s)
+      if (d->segs[s].len > 0) order.push_back(s);
+    if (!sorted)
+      std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        return d->segs[x].pos_start < d->segs[y].pos_start;
+      });
     for (size_t i = 1; i < order.size(); ++i) {
       const msa_segment& p = d->segs[order[i - 1]];
       const msa_segment& c = d->segs[order[i]];
       if ((int64_t)p.pos_start + p.len > c.pos_start)
-        return fail(err, INV, "sequence %d: segments %d and %d overlap in position", b,
-                    order[i - 1], order[i]);
+        return fail(err, INV, "sequence %d: segments %d and %d overlap in position", b, order[i - 1],
+                    order[i]);
     }
-    const int32_t seq_blk0 = (int32_t)plan.blocks.size();
+    const int32_t seq_blk0 = cursor;
+    BlockEntry* dst = plan.blocks.data();
     for (int32_t s : order) {
-      const msa_segment& sg = d->segs[s];
-      for (int32_t j = 0; j * kBlock < sg.len; ++j) {
-        const int32_t valid = std::min(kBlock, sg.len - j * kBlock);
-        BlockEntry e;
-        e.bt_valid = (int32_t)((uint32_t)(sg.bt_start + j) | ((uint32_t)(valid - 1) << kBtIndexBits));
-        e.pos0 = sg.pos_start + j * kBlock;
-        plan.blocks.push_back(e);
+      // locals, so that the stores below need not reload the segment
+      const int32_t len = d->segs[s].len, pos = d->segs[s].pos_start, bt = d->segs[s].bt_start;
+      const int32_t full = len / kBlock, tail = len - full * kBlock;
+      const uint32_t full_tag = (uint32_t)(kBlock - 1) << kBtIndexBits;
+      BlockEntry* out = dst + cursor;
+      int32_t tag = (int32_t)((uint32_t)bt | full_tag), p0 = pos;
+      for (int32_t j = 0; j < full; ++j, ++tag, p0 += kBlock) {
+        out[j].bt_valid = tag;
+        out[j].pos0 = p0;
       }
+      cursor += full;
+      if (tail)
+        dst[cursor++] = BlockEntry{(int32_t)((uint32_t)(bt + full) | ((uint32_t)(tail - 1) << kBtIndexBits)),
+                                   pos + full * kBlock};
     }
-    const int32_t seq_blk1 = (int32_t)plan.blocks.size();
+    const int32_t seq_blk1 = cursor;
 
     // Query tiles of this sequence.
     const int32_t q0 = d->q_offsets[b], q1 = d->q_offsets[b + 1];
@@ -164,11 +222,11 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
       }
       if (d->causal) {
         // first block whose slot-0 position is beyond every query of the tile
-        auto it = std::upper_bound(plan.blocks.begin() + seq_blk0, plan.blocks.begin() + seq_blk1,
-                                   qmax, [](int32_t v, const BlockEntry& e) { return v < e.pos0; });
+        auto it = std::upper_bound(plan.blocks.begin() + seq_blk0, plan.blocks.begin() + seq_blk1, qmax,
+                                   [](int32_t v, const BlockEntry& e) { return v < e.pos0; });
         end = (int32_t)(it - plan.blocks.begin());
       }
-      tiles.push_back(Tile{kind, b, qmin, r, n, seq_blk0, end});
+      tiles.push_back(Tile{kind, b, qmin, r, n, seq_blk0, end, 1});
     }
   }
   plan.q_pos.assign(d->q_pos, d->q_pos + total_q);
@@ -180,43 +238,62 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   for (int k = 0; k < 3; ++k)
     chunk[k] = cfg.split_blocks > 0 ? cfg.split_blocks : auto_chunk(k, total_blocks[k], cfg.num_cus);
 
-  for (const Tile& t : tiles) {
+  // Split count of every tile, then the item and merge counts, so that the
+  // lists are sized once and written in place.
+  size_t n_items[3] = {0, 0, 0}, n_merges = 0;
+  int64_t part_rows = 0;
+  for (Tile& t : tiles) {
     const int32_t nblk = t.blk_end - t.blk_begin;
     const int64_t c = chunk[t.kind];
     int32_t nsplit = 1;
-    if (cfg.split_blocks > 0 ? nblk > c : nblk > c + c / 2)
-      nsplit = (int32_t)((nblk + c - 1) / c);
+    if (cfg.split_blocks > 0 ? nblk > c : nblk > c + c / 2) nsplit = (int32_t)((nblk + c - 1) / c);
     const int32_t align = (t.kind == kPrefill) ? 4 : 1;  // prefill consumes 4 blocks per step
-    nsplit = std::min(nsplit, (nblk + align - 1) / align);
-    if (nsplit < 1) nsplit = 1;
+    nsplit = std::max(1, std::min(nsplit, (nblk + align - 1) / align));
+    t.nsplit = nsplit;
     const int32_t n_mrows = t.n_q * group;
     plan.max_mrows[t.kind] = std::max(plan.max_mrows[t.kind], n_mrows);
-    for (int32_t h = 0; h < cfg.num_kv_heads; ++h) {
-      if (nsplit == 1) {
-        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, t.q_min});
-        continue;
-      }
-      if ((int64_t)plan.part_rows + (int64_t)nsplit * n_mrows > std::numeric_limits<int32_t>::max())
-        return fail(err, MSA_ERR_WORKSPACE, "split partials exceed 2^31 rows");
-      const int32_t part0 = (int32_t)plan.part_rows;
-      const int32_t units = (nblk + align - 1) / align;
-      int32_t done = 0;
-      for (int32_t s = 0; s < nsplit; ++s) {
-        const int32_t u1 = (int32_t)((int64_t)units * (s + 1) / nsplit);
-        const int32_t b1 = std::min(nblk, u1 * align);
-        plan.items[t.kind].push_back(WorkItem{h, t.q_row0, t.n_q, t.blk_begin + done,
-                                              t.blk_begin + b1, part0 + s * n_mrows, t.seq, t.q_min});
-        done = b1;
-      }
-      plan.merges.push_back(MergeItem{h, t.q_row0, t.n_q, part0, nsplit, n_mrows, 0, 0});
-      plan.part_rows += (int64_t)nsplit * n_mrows;
+    n_items[t.kind] += (size_t)nsplit * cfg.num_kv_heads;
+    if (nsplit > 1) {
+      n_merges += cfg.num_kv_heads;
+      part_rows += (int64_t)nsplit * n_mrows * cfg.num_kv_heads;
     }
   }
-  // Largest work first, so the tail of the launch is made of small items.
-  for (auto& v : plan.items)
-    std::stable_sort(v.begin(), v.end(), [](const WorkItem& x, const WorkItem& y) {
-      return (x.blk_end - x.blk_begin) > (y.blk_end - y.blk_begin);
-    });
+  if (part_rows > std::numeric_limits<int32_t>::max())
+    return fail(err, MSA_ERR_WORKSPACE, "split partials exceed 2^31 rows");
+  for (int k = 0; k < 3; ++k) plan.items[k].resize(n_items[k]);
+  plan.merges.resize(n_merges);
+  WorkItem* item_out[3] = {plan.items[0].data(), plan.items[1].data(), plan.items[2].data()};
+  MergeItem* merge_out = plan.merges.data();
+  std::vector<int32_t>& bounds = plan_order();  // reused: split boundaries of one tile
+  int32_t part = 0;
+  for (const Tile& t : tiles) {
+    WorkItem*& wo = item_out[t.kind];
+    if (t.nsplit == 1) {
+      for (int32_t h = 0; h < cfg.num_kv_heads; ++h)
+        *wo++ = WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, t.q_min};
+      continue;
+    }
+    // the same block ranges for every kv head
+    const int32_t nblk = t.blk_end - t.blk_begin;
+    const int32_t align = (t.kind == kPrefill) ? 4 : 1;
+    const int32_t units = (nblk + align - 1) / align;
+    bounds.resize((size_t)t.nsplit + 1);
+    bounds[0] = 0;
+    for (int32_t s = 0; s < t.nsplit; ++s)
+      bounds[s + 1] = std::min(nblk, (int32_t)((int64_t)units * (s + 1) / t.nsplit) * align);
+    const int32_t n_mrows = t.n_q * group;
+    for (int32_t h = 0; h < cfg.num_kv_heads; ++h) {
+      for (int32_t s = 0; s < t.nsplit; ++s)
+        *wo++ = WorkItem{h, t.q_row0, t.n_q, t.blk_begin + bounds[s], t.blk_begin + bounds[s + 1],
+                         part + s * n_mrows, t.seq, t.q_min};
+      *merge_out++ = MergeItem{h, t.q_row0, t.n_q, part, t.nsplit, n_mrows, 0, 0};
+      part += t.nsplit * n_mrows;
+    }
+  }
+  plan.part_rows = part;
+  // Largest work first, so the tail of the launch is made of small items;
+  // items of equal size keep their order.
+  for (auto& v : plan.items) sort_by_size(v);
   return MSA_OK;
 }
 

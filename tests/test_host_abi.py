@@ -217,6 +217,23 @@ def test_planner_exact_coverage_fp32_and_noncausal():
     check_plan(wl2, split_blocks=2)
 
 
+def test_planner_ordered_and_shuffled_segments_agree():
+    # the planner sorts a sequence's segments only when they arrive out of
+    # position order; both inputs must give the same block list and items
+    spec = [([(0, 40), (48, 33), (100, 7), (300, 64)], [10, 120, 363]), ([(5, 17), (30, 1)], [30])]
+    plans = []
+    for shuffle in (False, True):
+        wl = W.custom(spec, H_q=4, H_kv=2, d=64, shuffle=shuffle, seed=3)
+        if not shuffle:
+            for b in range(wl.batch):
+                p = wl.segs[wl.seg_offsets[b]:wl.seg_offsets[b + 1], 0]
+                assert list(p) == sorted(p)
+        items, blocks = check_plan(wl, split_blocks=2)
+        plans.append(([(p0, v) for (_bt, p0, v) in blocks], sorted(
+            (int(it["kv_head"]), int(it["q_row0"]), int(it["blk_begin"]), int(it["blk_end"])) for it in items)))
+    assert plans[0] == plans[1]
+
+
 def test_planner_kinds_and_lpt_order():
     wl = W.custom([([(0, 100)], [99]), ([(0, 300)], list(range(300, 340)))], H_q=8, H_kv=2, d=128)
     items, _ = check_plan(wl)
