@@ -9,10 +9,11 @@
 // Per step of 64 keys (4 pool blocks of the position-ordered block list, which
 // may span segment boundaries):
 //   * the next step's K and V are fetched from HBM into registers (16-byte
-//     loads; one block's 4 KiB are contiguous) while this step computes, then
-//     written to the other LDS buffer: K row-major with 16-byte chunks XOR-
-//     swizzled, V transposed (head_dim rows of 64 keys) so that the PV operand
-//     is a 16-byte LDS read;
+//     buffer loads, one buffer resource per pool block, whose 4 KiB per kv
+//     head are contiguous) while this step computes, then written to the
+//     other LDS buffer: K row-major with 16-byte chunks XOR-swizzled, V
+//     transposed (head_dim rows of 64 keys) so that the PV operand is a
+//     16-byte LDS read;
 //   * S^T = K Q^T (K from LDS, Q^T resident in registers), so each lane holds
 //     one tile row's scores for 16 keys;
 //   * keys outside a block's valid slots, past the item's blocks, or (causal)
@@ -38,11 +39,10 @@ constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
 constexpr float kRefSumLimit = 1048576.f;  // 2^20: largest accepted partial row sum per step
 
-// LDS tiles.  gfx950's LDS serves a ds_read_b128 16 lanes per clock (64 banks
-// x 4 bytes), so an operand read is conflict-free when the 16 lanes of each
-// quarter-wave hit 16 distinct 16-byte bank groups.  Operand reads touch 16
-// consecutive rows at one chunk index; the XOR swizzles below spread those
-// over all bank groups.
+// LDS tiles.  Operand reads touch 32 consecutive rows at one chunk index; the
+// XOR swizzles below were chosen by measurement on gfx950 so that those reads
+// run at the rate of a contiguous ds_read_b128 (about 4.4 clocks per wave
+// instruction per CU) and the staging writes at the rate of contiguous writes.
 template <int D>
 struct PrefillSmem {
   uint4 k[2][kStepKeys][D / 8];   // [buf][key][chunk]: K rows (head_dim), swizzled
@@ -56,10 +56,10 @@ __device__ __forceinline__ int k_swz(int row) {
   if constexpr (D == 128) return row & 15;
   else return (row >> 1) & 7;
 }
-// Vt rows are 128 bytes: distinct positions for each parity class of 16
-// aligned rows (operand reads), and for 8 rows spaced 8 apart (the
-// transposed writes of one quarter-wave).
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 7; }
+// Vt rows are 128 bytes.  With (d >> 1) ^ (d >> 4) both the operand reads and
+// the transposed staging writes (rows 8 apart) are conflict-free; the
+// (d >> 1) ^ (d >> 3) variant halves the operand-read rate.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 
 // Position of local key k (0..63) inside a transposed V row: bits 2 and 3 of
 // k are swapped so that the 8 keys one lane feeds to the PV MFMA are adjacent.
@@ -126,34 +126,41 @@ struct StepRegs {
 // later (K: masked scores, V: zeroed when staged).  K and V are fetched at
 // different points of a step so that their staging registers are not live
 // at the same time.
+// One pool block of one kv head as a buffer resource (scalar registers):
+// loads take a 32-bit lane offset, and offsets past the block read zero.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* pool, int kv_head, int num_kv_heads, int phys) {
+  const char* p = (const char*)pool + ((int64_t)phys * num_kv_heads + kv_head) * (kBlock * D * 2);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, kBlock * D * 2, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <int D>
 __device__ __forceinline__ void fetch_k(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
   constexpr int CPR = D / 8;  // 16-byte chunks per key row
-  const bf16_t* __restrict__ K = (const bf16_t*)a.k;
-  const int64_t head_off = (int64_t)kv_head * (kBlock * D);
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * (kBlock * D);
+  // D = 128: chunk i*256+t is block i, row t/16, chunk t%16.
+  // D = 64:  chunk i*256+t is block 2i + t/128, row (t/8)%16, chunk t%8.
+  const uint32_t off = (D == 128) ? (uint32_t)t * 16u : (uint32_t)(((t >> 3) & 15) * D + (t % CPR) * 8) * 2u;
+  const int half = __builtin_amdgcn_readfirstlane(t >> 7);
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
-    // D = 128: chunk i*256+t is block i, row t/16, chunk t%16.
-    // D = 64:  chunk i*256+t is block 2i + t/128, row (t/8)%16, chunk t%8.
-    const int b = (D == 128) ? i : 2 * i + (t >> 7);
-    const int slot = (D == 128) ? (t >> 4) : ((t >> 3) & 15);
-    const int c = t % CPR;
-    r.k[i] = *(const uint4*)(K + m.phys(b) * blk_stride + head_off + slot * D + c * 8);
+    const int b = (D == 128) ? i : 2 * i + half;
+    r.k[i] = buf_load16(block_rsrc<D>(a.k, kv_head, a.num_kv_heads, m.phys(b)), off);
   }
 }
 template <int D>
 __device__ __forceinline__ void fetch_v(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
   constexpr int CPR = D / 8;
   constexpr int KPT = D / 32;            // keys per thread for V
-  const bf16_t* __restrict__ V = (const bf16_t*)a.v;
-  const int64_t head_off = (int64_t)kv_head * (kBlock * D);
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * (kBlock * D);
   const int c = t % CPR, kg = t / CPR;
-  const int b = (kg * KPT) >> 4, slot0 = (kg * KPT) & 15;
-  const bf16_t* vsrc = V + m.phys(b) * blk_stride + head_off + slot0 * D + c * 8;
+  // a wave's keys lie in one block: D = 128, block = wave; D = 64, wave / 2
+  const int b = __builtin_amdgcn_readfirstlane((kg * KPT) >> 4);
+  const uint32_t off = (uint32_t)(((kg * KPT) & 15) * D + c * 8) * 2u;
+  const __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(a.v, kv_head, a.num_kv_heads, m.phys(b));
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) r.v[e] = *(const uint4*)(vsrc + e * D);
+  for (int e = 0; e < KPT; ++e) r.v[e] = buf_load16(rs, off + e * D * 2);
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& u, int w) {
@@ -164,13 +171,13 @@ __device__ __forceinline__ uint32_t word_of(const uint4& u, int w) {
 // slots without a key written as zero on steps that are not full.
 template <int D>
 __device__ __forceinline__ void stage_k(PrefillSmem<D>& sm, int buf, const StepRegs<D>& r, int t) {
+  // Chunk i*256+t goes to row i*(4096/(2D)) + t/CPR; the swizzle of that row
+  // does not depend on i, so the rows of one lane are 4 KiB apart.
   constexpr int CPR = D / 8;
+  const int row = t / CPR, c = t % CPR;
+  char* dst = (char*)&sm.k[buf][row][c ^ k_swz<D>(row)];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int id = i * kThreads + t;
-    const int row = id / CPR, c = id % CPR;
-    sm.k[buf][row][c ^ k_swz<D>(row)] = r.k[i];
-  }
+  for (int i = 0; i < D / 32; ++i) *(uint4*)(dst + i * 4096) = r.k[i];
 }
 template <int D>
 __device__ __forceinline__ void stage_v(PrefillSmem<D>& sm, int buf, StepRegs<D>& r, const StepMeta& m, int t) {
@@ -178,11 +185,18 @@ __device__ __forceinline__ void stage_v(PrefillSmem<D>& sm, int buf, StepRegs<D>
   constexpr int KPT = D / 32;
   const int c = t % CPR, kg = t / CPR;
   if (!m.full) {
-    const int b = (kg * KPT) >> 4, slot0 = (kg * KPT) & 15;
+    // a wave's keys lie in one block
+    const int b = __builtin_amdgcn_readfirstlane((kg * KPT) >> 4);
     const int valid = b < m.nb ? m.valid(b) : 0;
+    const int slot0 = (kg * KPT) & 15;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-      if (slot0 + e >= valid) r.v[e] = make_uint4(0, 0, 0, 0);
+    for (int e = 0; e < KPT; ++e) {
+      const bool dead = slot0 + e >= valid;
+      r.v[e].x = dead ? 0u : r.v[e].x;
+      r.v[e].y = dead ? 0u : r.v[e].y;
+      r.v[e].z = dead ? 0u : r.v[e].z;
+      r.v[e].w = dead ? 0u : r.v[e].w;
+    }
   }
   const int kpos = vt_key_pos(kg * KPT);
   const int chunk = kpos >> 3;
