@@ -121,7 +121,8 @@ typedef struct {
  *
  *  q            device [total_q][num_q_heads][head_dim], pool dtype
  *  block_table  device int32 [block_table_len]; entries are pool block ids in
- *               [0, num_blocks) (not range-checked on the device)
+ *               [0, num_blocks), read on `stream` (an id out of range is
+ *               clamped into the pool on the device, not reported)
  *  out          device [total_q][num_q_heads][head_dim], pool dtype
  *  lse          device float32 [total_q][num_q_heads], or NULL
  *  stream       hipStream_t to enqueue on (NULL = default stream)

@@ -152,6 +152,60 @@ def test_deterministic():
         case.close()
 
 
+def test_back_to_back_calls_with_changing_plans():
+    # Plans of consecutive calls alternate between two device buffers, copied
+    # on the pool's upload stream; calls are queued without a host sync in
+    # between and their plans differ in size (the buffers grow on the way).
+    wl = W.random_case(62, batch=4, H_q=32, H_kv=8, d=128, max_ctx=700)
+    case = GpuCase(wl)
+    splits = [0, 3, 1, 7, 0, 2, 1]
+    outs = []
+    try:
+        for sb in splits:
+            case.pool.set_option(msa.OPT_SPLIT_BLOCKS, sb)
+            o = torch.full_like(case.q, float("nan"))
+            l = torch.full((wl.total_q, wl.num_q_heads), float("nan"), device="cuda")
+            msa.forward(case.q, case.desc, case.bt, case.pool, o, l)
+            outs.append((o, l))
+        torch.cuda.synchronize()
+    finally:
+        case.close()
+    ref_out, ref_lse = oracle_result(wl)
+    for sb, (o, l) in zip(splits, outs):
+        print(f"[parity] back-to-back split_blocks={sb}", flush=True)
+        compare(wl, o.cpu(), l.cpu(), ref_out, ref_lse)
+
+
+def test_block_table_written_on_the_stream_between_calls():
+    # The kernels read pool block ids through the block table on the call's
+    # stream: a table rewritten on that stream between two calls is honoured.
+    wl = W.random_case(63, batch=3, H_q=8, H_kv=2, d=128, max_ctx=500)
+    K, V = wl.dense_pool("cuda")
+    nb = K.shape[0]
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(nb)).cuda()
+    K2 = torch.empty_like(K)
+    V2 = torch.empty_like(V)
+    K2[perm] = K
+    V2[perm] = V
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K2, v=V2)
+    try:
+        bt_old = torch.from_numpy(wl.block_table.astype(np.int64)).cuda()
+        bt = bt_old.to(torch.int32)                 # ids of the unpermuted pool: wrong for K2
+        q = wl.q.cuda()
+        desc = msa.SegDesc.from_workload(wl)
+        o1 = torch.empty_like(q)
+        o2 = torch.full_like(q, float("nan"))
+        l2 = torch.full((wl.total_q, wl.num_q_heads), float("nan"), device="cuda")
+        msa.forward(q, desc, bt, pool, o1, None)
+        bt.copy_(perm[bt_old].to(torch.int32))     # enqueued on the same stream
+        msa.forward(q, desc, bt, pool, o2, l2)
+        torch.cuda.synchronize()
+    finally:
+        pool.close()
+    ref_out, ref_lse = oracle_result(wl)
+    compare(wl, o2.cpu(), l2.cpu(), ref_out, ref_lse)
+
+
 def test_library_allocated_pool():
     wl = W.random_case(61, batch=2, H_q=8, H_kv=2, d=128)
     pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16)
