@@ -144,6 +144,9 @@ class SegDesc:
         self.q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
         self.seg_offsets = np.ascontiguousarray(seg_offsets, dtype=np.int32)
         self.segs = np.ascontiguousarray(np.asarray(segs, dtype=np.int32).reshape(-1, 4))
+        self.total_q = int(self.q_offsets[-1]) if len(self.q_offsets) else 0
+        self.num_q_heads = int(num_q_heads)
+        self.block_table_len = int(block_table_len)
         self.c = _SegDesc(len(self.q_offsets) - 1, int(num_q_heads),
                           self.q_offsets.ctypes.data, self.q_pos.ctypes.data,
                           self.seg_offsets.ctypes.data, self.segs.ctypes.data,
@@ -215,11 +218,43 @@ def forward(q, seg_desc: SegDesc, block_table, pool: Pool, out, lse=None, stream
     """Enqueue MSA for one batch on ``stream`` (default: torch's current stream).
 
     ``q``/``out``: [total_q, num_q_heads, head_dim] device tensors of the pool
-    dtype; ``block_table``: int32 device tensor; ``lse``: float32
-    [total_q, num_q_heads] device tensor or None.
+    dtype (more rows are allowed; rows past total_q are not touched);
+    ``block_table``: int32 device tensor; ``lse``: float32 [total_q,
+    num_q_heads] device tensor or None.
     """
+    _check_forward_tensors(q, seg_desc, block_table, pool, out, lse)
     _check(load_library().msa_forward(_ptr(q), ctypes.byref(seg_desc.c), _ptr(block_table), pool.handle,
                                       _ptr(out), _ptr(lse), _current_stream(stream)))
+
+
+def _is_tensor(x) -> bool:
+    return hasattr(x, "data_ptr") and hasattr(x, "shape")
+
+
+def _check_forward_tensors(q, d: SegDesc, block_table, pool: Pool, out, lse):
+    """Shape, dtype and layout checks of the torch tensors handed to msa_forward
+    (the C ABI receives bare pointers and cannot check sizes).  Raw integer
+    addresses are passed through unchecked."""
+    if d.total_q == 0:
+        return
+    # Row counts may exceed total_q (buffers sized for a larger batch).
+    rows, inner = d.total_q, (d.num_q_heads, pool.head_dim)
+    elt = 4 if pool.dtype == FP32 else 2
+    for name, t in (("q", q), ("out", out)):
+        if _is_tensor(t):
+            if (t.dim() != 3 or t.shape[0] < rows or tuple(t.shape[1:]) != inner or not t.is_contiguous()
+                    or t.element_size() != elt or not t.is_cuda):
+                raise ValueError(f"{name} must be a contiguous device tensor [>= {rows}, {inner[0]}, {inner[1]}] "
+                                 "of the pool dtype")
+    if _is_tensor(lse):
+        if (lse.dim() != 2 or lse.shape[0] < rows or lse.shape[1] != inner[0] or not lse.is_contiguous()
+                or lse.element_size() != 4 or not lse.dtype.is_floating_point or not lse.is_cuda):
+            raise ValueError(f"lse must be a contiguous float32 device tensor [>= {rows}, {inner[0]}]")
+    if _is_tensor(block_table):
+        if (block_table.element_size() != 4 or block_table.dtype.is_floating_point or not block_table.is_cuda
+                or not block_table.is_contiguous() or block_table.numel() < d.block_table_len):
+            raise ValueError("block_table must be a contiguous int32 device tensor of at least "
+                             f"block_table_len = {d.block_table_len} entries")
 
 
 def write_kv(pool: Pool, k_src, v_src, segs, src_rows, block_table, stream=None):

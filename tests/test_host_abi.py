@@ -343,3 +343,22 @@ def test_kernel_time_and_samples_argument_checks():
         assert lib.msa_pool_set_option(h, 77, 1) == msa.ERR_INVALID_ARG
     finally:
         lib.msa_destroy_pool(h)
+
+
+def test_binding_checks_tensor_shapes_before_the_library():
+    # The C ABI gets bare pointers; the Python binding rejects tensors whose
+    # shape, dtype, layout or device cannot match the descriptor, before any
+    # library call (a pool stand-in with the attributes the check reads).
+    import types
+    import torch
+    d = msa.SegDesc([0, 3], [5, 6, 7], [0, 1], [[0, 8, 0, 0]], 1, num_q_heads=4)
+    pool = types.SimpleNamespace(head_dim=64, dtype=msa.BF16, handle=None)
+    good_q = torch.zeros(3, 4, 64, dtype=torch.bfloat16)        # right shape, but host memory
+    with pytest.raises(ValueError, match="q must be"):
+        msa.forward(good_q, d, 0x2000, pool, 0x3000)
+    with pytest.raises(ValueError, match="out must be"):
+        msa.forward(0x1000, d, 0x2000, pool, torch.zeros(3, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must be"):
+        msa.forward(0x1000, d, 0x2000, pool, 0x3000, torch.zeros(3, 5))
+    with pytest.raises(ValueError, match="block_table must be"):
+        msa.forward(0x1000, d, torch.zeros(1, dtype=torch.int64), pool, 0x3000)
