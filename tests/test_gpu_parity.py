@@ -82,6 +82,10 @@ def test_edge_cases():
         W.custom([([(0, 1000)], [997, 998, 999])], H_q=16, H_kv=2, d=128, seed=7),
         # explicit scale
         W.custom([([(0, 77)], list(range(60, 77)))], H_q=4, H_kv=1, d=128, seed=8, scale=0.05),
+        # largest GQA ratio (128 q heads on one kv head: one token per 128-row chunk tile), and a
+        # decode token whose group (16) exceeds the decode kernel's 8 rows
+        W.custom([([(0, 90), (100, 40)], [139, 120, 95])], H_q=128, H_kv=1, d=64, seed=9),
+        W.custom([([(0, 500)], [499]), ([(0, 33)], [32])], H_q=32, H_kv=2, d=128, seed=10),
     ]
     for wl in cases:
         _check(wl)
