@@ -8,23 +8,24 @@
 //
 // Per step of 64 keys (4 pool blocks of the position-ordered block list, which
 // may span segment boundaries):
-//   * the next step's K and V are fetched from HBM into registers (16-byte
-//     buffer loads, one buffer resource per pool block, whose 4 KiB per kv
-//     head are contiguous) while this step computes, then written to the
-//     other LDS buffer: K row-major with 16-byte chunks XOR-swizzled, V
-//     transposed (head_dim rows of 64 keys) so that the PV operand is a
-//     16-byte LDS read;
 //   * S^T = K Q^T (K from LDS, Q^T resident in registers), so each lane holds
 //     one tile row's scores for 16 keys;
+//   * then the next step's K and V go from the pool straight into the other
+//     LDS tile by LDS DMA (buffer loads with the lds flag, one buffer
+//     resource per pool block, whose 4 KiB per kv head are contiguous; each
+//     wave moves one block), so staging costs the waves neither registers
+//     nor LDS writes, and has the rest of the step to land;
 //   * keys outside a block's valid slots, past the item's blocks, or (causal)
 //     at a position after the row's query position get score -inf by select;
 //     steps that are entirely visible to every row skip the mask;
 //   * online softmax in the exp2 domain (scale * log2 e folded into one FMA)
 //     against a per-row reference that moves only when needed;
 //   * P is rounded to bf16 in place of the S accumulator registers and used as
-//     the B operand of O^T += V^T P^T.
-// Slots that hold no key are zero-filled in LDS, so the 0-probabilities never
-// meet pool contents (NaN * 0 would poison the row).
+//     the B operand of O^T += V^T P^T, whose V^T operand comes from the
+//     row-major V tile through the transposing LDS read of gfx950.
+// Each block's buffer resource covers only its valid slots: DMA reads past
+// them return zero, so slots that hold no key are zero in LDS and the
+// 0-probabilities never meet pool contents (NaN * 0 would poison the row).
 #include "msa_common.h"
 
 namespace msa {
@@ -39,32 +40,30 @@ constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
 constexpr float kRefSumLimit = 1048576.f;  // 2^20: largest accepted partial row sum per step
 
-// LDS tiles.  Operand reads touch 32 consecutive rows at one chunk index; the
-// XOR swizzles below were chosen by measurement on gfx950 so that those reads
-// run at the rate of a contiguous ds_read_b128 (about 4.4 clocks per wave
-// instruction per CU) and the staging writes at the rate of contiguous writes.
+// LDS tiles, one per buffer (two separate LDS variables, so that the
+// compiler can tell reads of one from DMA writes into the other).  Both K
+// and V are stored row-major (one key per row) with their 16-byte chunks
+// XOR-swizzled, and are filled by LDS DMA straight from the pool.
 template <int D>
-struct PrefillSmem {
-  uint4 k[2][kStepKeys][D / 8];   // [buf][key][chunk]: K rows (head_dim), swizzled
-  uint4 vt[2][D][kStepKeys / 8];  // [buf][d][chunk]: V transposed (64 keys), swizzled
+struct StepTile {
+  uint4 k[kStepKeys][D / 8];   // [key][chunk]: K rows, chunk c at c ^ k_swz(key)
+  uint4 v[kStepKeys][D / 8];   // [key][chunk]: V rows, chunk c at c ^ v_swz(key)
 };
 
-// K rows are 256 bytes (D=128: one row covers all banks) or 128 bytes (D=64:
-// rows of one parity share a bank half).
+// K operand reads take 32 consecutive rows at one chunk index: with the row
+// XOR the 16-byte reads of a wave spread over all banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   if constexpr (D == 128) return row & 15;
   else return (row >> 1) & 7;
 }
-// Vt rows are 128 bytes.  With (d >> 1) ^ (d >> 4) both the operand reads and
-// the transposed staging writes (rows 8 apart) are conflict-free; the
-// (d >> 1) ^ (d >> 3) variant halves the operand-read rate.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
-
-// Position of local key k (0..63) inside a transposed V row: bits 2 and 3 of
-// k are swapped so that the 8 keys one lane feeds to the PV MFMA are adjacent.
-__device__ __forceinline__ int vt_key_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// V operand reads (ds_read_b64_tr_b16) take, per half-wave, 64 bytes (32
+// head_dim values) of 4 consecutive rows; the XOR moves each of the 4 rows
+// to its own quarter of the banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  if constexpr (D == 128) return (row & 3) << 2;
+  else return (row & 2) << 1;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -75,12 +74,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8 ld_k(const PrefillSmem<D>& sm, int buf, int row, int c) {
-  return as_bf16x8(sm.k[buf][row][c ^ k_swz<D>(row)]);
+__device__ __forceinline__ bf16x8 ld_k(const StepTile<D>& tl, int row, int c) {
+  return as_bf16x8(tl.k[row][c ^ k_swz<D>(row)]);
 }
-template <int D>
-__device__ __forceinline__ bf16x8 ld_vt(const PrefillSmem<D>& sm, int buf, int d, int c) {
-  return as_bf16x8(sm.vt[buf][d][c ^ vt_swz(d)]);
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, component r of lane i's result is 16-bit element i % 4 of the 8
+// bytes addressed by lane 4r + i / 4 of the group.
+__device__ __forceinline__ s16x4 ld_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<char*>(p)));
 }
 
 // Descriptors of one step's (up to) 4 blocks.  Plain scalar fields rather
@@ -99,7 +105,7 @@ struct StepMeta {
 // The block list is padded with 4 spare entries and indices are clamped to
 // them, so the entries of any step (also one past the item's last) are
 // readable; entries past the item's end get valid = 0 (their ids are still
-// pool block ids, so loads from them stay in bounds).
+// pool block ids).
 __device__ __forceinline__ void load_meta(const KernelArgs& a, int blk, int blk_end, int q_min, StepMeta& m) {
   m.nb = max(0, min(4, blk_end - blk));
   const int last = blk_end + 3;
@@ -115,104 +121,59 @@ __device__ __forceinline__ void load_meta(const KernelArgs& a, int blk, int blk_
            (!a.causal || m.ps3 + 15 <= q_min);
 }
 
+// The valid rows of one pool block of one kv head as a buffer resource:
+// loads past them (slots without a key, whole blocks past the item's end)
+// read zero, so no pool contents outside the keys reach LDS.
 template <int D>
-struct StepRegs {
-  uint4 k[D / 32];   // D=128: 4 chunks, D=64: 2 chunks
-  uint4 v[D / 32];   // keys-per-thread of one 16-byte d chunk
-};
-
-// Global -> registers for one step.  Every load is in bounds (block ids of
-// the step are pool ids, slots 0..15); slots that hold no key are dealt with
-// later (K: masked scores, V: zeroed when staged).  K and V are fetched at
-// different points of a step so that their staging registers are not live
-// at the same time.
-// One pool block of one kv head as a buffer resource (scalar registers):
-// loads take a 32-bit lane offset, and offsets past the block read zero.
-template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* pool, int kv_head, int num_kv_heads, int phys) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* pool, int kv_head, int num_kv_heads, int phys,
+                                                             int valid) {
   const char* p = (const char*)pool + ((int64_t)phys * num_kv_heads + kv_head) * (kBlock * D * 2);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, kBlock * D * 2, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, valid * D * 2, 0x00020000);
 }
 
+// Per-lane byte offsets (inside a pool block) of the 16-byte chunks that the
+// DMA of one step brings in.  One DMA instruction fills 1 KiB of LDS, lane j
+// at byte 16 j, i.e. (D = 128) row 4i + j/16 of the block, physical chunk
+// j % 16; the lane fetches the logical chunk that belongs there.
 template <int D>
-__device__ __forceinline__ void fetch_k(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per key row
-  // D = 128: chunk i*256+t is block i, row t/16, chunk t%16.
-  // D = 64:  chunk i*256+t is block 2i + t/128, row (t/8)%16, chunk t%8.
-  const uint32_t off = (D == 128) ? (uint32_t)t * 16u : (uint32_t)(((t >> 3) & 15) * D + (t % CPR) * 8) * 2u;
-  const int half = __builtin_amdgcn_readfirstlane(t >> 7);
+struct DmaOffsets {
+  uint32_t k[D / 32];
+  uint32_t v;               // + i KiB for instruction i
+};
+template <int D>
+__device__ __forceinline__ DmaOffsets<D> dma_offsets(int lane) {
+  constexpr int CPR = D / 8;      // chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per instruction
+  DmaOffsets<D> o;
+  const int p = lane % CPR, r = lane / CPR;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
-    const int b = (D == 128) ? i : 2 * i + half;
-    r.k[i] = buf_load16(block_rsrc<D>(a.k, kv_head, a.num_kv_heads, m.phys(b)), off);
+    const int row = i * RPI + r;  // row inside the block (the block's base row is a multiple of 16)
+    o.k[i] = (uint32_t)(row * CPR + (p ^ k_swz<D>(row))) * 16u;
   }
-}
-template <int D>
-__device__ __forceinline__ void fetch_v(const KernelArgs& a, int kv_head, const StepMeta& m, StepRegs<D>& r, int t) {
-  constexpr int CPR = D / 8;
-  constexpr int KPT = D / 32;            // keys per thread for V
-  const int c = t % CPR, kg = t / CPR;
-  // a wave's keys lie in one block: D = 128, block = wave; D = 64, wave / 2
-  const int b = __builtin_amdgcn_readfirstlane((kg * KPT) >> 4);
-  const uint32_t off = (uint32_t)(((kg * KPT) & 15) * D + c * 8) * 2u;
-  const __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(a.v, kv_head, a.num_kv_heads, m.phys(b));
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) r.v[e] = buf_load16(rs, off + e * D * 2);
+  o.v = (uint32_t)(r * CPR + (p ^ v_swz<D>(r))) * 16u;  // v_swz depends on row % 4 only
+  return o;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int w) {
-  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
-}
-
-// Registers -> LDS buffer: K row-major swizzled; V transposed, with V rows of
-// slots without a key written as zero on steps that are not full.
+// One step's K and V of block `wave` (each wave moves one of the 4 blocks)
+// from the pool into a tile by LDS DMA.
 template <int D>
-__device__ __forceinline__ void stage_k(PrefillSmem<D>& sm, int buf, const StepRegs<D>& r, int t) {
-  // Chunk i*256+t goes to row i*(4096/(2D)) + t/CPR; the swizzle of that row
-  // does not depend on i, so the rows of one lane are 4 KiB apart.
+__device__ __forceinline__ void dma_step(const KernelArgs& a, int kv_head, const StepMeta& m, StepTile<D>& tl,
+                                         int wave, const DmaOffsets<D>& o) {
   constexpr int CPR = D / 8;
-  const int row = t / CPR, c = t % CPR;
-  char* dst = (char*)&sm.k[buf][row][c ^ k_swz<D>(row)];
+  constexpr int RPI = 64 / CPR;
+  const int phys = m.phys(wave), valid = m.valid(wave);
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(a.k, kv_head, a.num_kv_heads, phys, valid);
+  const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(a.v, kv_head, a.num_kv_heads, phys, valid);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) *(uint4*)(dst + i * 4096) = r.k[i];
-}
-template <int D>
-__device__ __forceinline__ void stage_v(PrefillSmem<D>& sm, int buf, StepRegs<D>& r, const StepMeta& m, int t) {
-  constexpr int CPR = D / 8;
-  constexpr int KPT = D / 32;
-  const int c = t % CPR, kg = t / CPR;
-  if (!m.full) {
-    // a wave's keys lie in one block
-    const int b = __builtin_amdgcn_readfirstlane((kg * KPT) >> 4);
-    const int valid = b < m.nb ? m.valid(b) : 0;
-    const int slot0 = (kg * KPT) & 15;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const bool dead = slot0 + e >= valid;
-      r.v[e].x = dead ? 0u : r.v[e].x;
-      r.v[e].y = dead ? 0u : r.v[e].y;
-      r.v[e].z = dead ? 0u : r.v[e].z;
-      r.v[e].w = dead ? 0u : r.v[e].w;
-    }
+  for (int i = 0; i < D / 32; ++i) {
+    const int off = (int)o.k[i];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&tl.k[16 * wave + i * RPI][0], 16, off, 0, 0, 0);
   }
-  const int kpos = vt_key_pos(kg * KPT);
-  const int chunk = kpos >> 3;
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int d = c * 8 + dd;
-    const int w = dd >> 1;
-    // bytes {0,1} (even dd) or {2,3} (odd dd) of word w of each key, low key first
-    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-    char* dst = (char*)&sm.vt[buf][d][chunk ^ vt_swz(d)] + (kpos & 7) * 2;
-    if constexpr (KPT == 4) {
-      *(uint2*)dst = make_uint2(__builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel),
-                                __builtin_amdgcn_perm(word_of(r.v[3], w), word_of(r.v[2], w), sel));
-    } else {
-      *(uint32_t*)dst = __builtin_amdgcn_perm(word_of(r.v[1], w), word_of(r.v[0], w), sel);
-    }
+  for (int i = 0; i < D / 32; ++i) {
+    const int off = (int)o.v + i * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&tl.v[16 * wave + i * RPI][0], 16, off, 0, 0, 0);
   }
 }
 
@@ -314,110 +275,145 @@ __device__ __forceinline__ void write_rows(const KernelArgs& a, const WorkItem& 
   }
 }
 
+// Per-lane byte offset, inside a tile's V rows, of the 8 bytes this lane
+// addresses for the V^T operand of head_dim block db (rows 16 ks (+8) are
+// added as immediates).  Lane L addresses row 4 (L / 32) + (L / 4) % 4 and
+// head_dim values 32 db + 16 ((L / 16) % 2) + 4 (L % 4) .. +4; after the
+// transposing read lane L holds, for d = 32 db + L % 32, the keys
+// 4 (L / 32) + 0..3 (first read) and 8 + 4 (L / 32) + 0..3 (second read) —
+// the keys whose probabilities the lane holds in P (see exp_half).
+template <int D>
+__device__ __forceinline__ uint32_t vtr_offset(int lane, int db) {
+  const int rr = (lane >> 2) & 3;
+  const int row = 4 * (lane >> 5) + rr;
+  const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  return (uint32_t)(row * 2 * D + ((chunk ^ v_swz<D>(rr)) << 4) + 8 * (lane & 1));
+}
+
+// Per-tile state of a lane across steps.
+template <int D>
+struct TileState {
+  bf16x8 qop[D / 16];     // Q^T operand: q[row][16ks + 8h .. +8) for every ks
+  f32x16 acc[D / 32];     // O^T accumulators
+  float m, l;             // per-row reference (log2 domain) and partial row sum
+};
+
+// One step of 64 keys on tile `tl`; the next step's K and V go into `nx` by
+// DMA meanwhile.  Ends with this wave's DMA complete and a work-group barrier.
+template <int D>
+__device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& it, const RowInfo& ri, TileState<D>& st,
+                                           const StepTile<D>& tl, StepTile<D>& nx, StepMeta& cur, StepMeta& nxt,
+                                           int next_blk, int wave, int lane, const DmaOffsets<D>& dof,
+                                           const uint32_t (&voff)[D / 32]) {
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const float c2 = a.scale_log2;
+
+  // ---- S^T = K Q^T for 64 keys ----
+  f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 k0 = ld_k<D>(tl, col, 2 * ks + h);
+    const bf16x8 k1 = ld_k<D>(tl, 32 + col, 2 * ks + h);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qop[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qop[ks], s1, 0, 0, 0);
+  }
+
+  dma_step<D>(a, it.kv_head, nxt, nx, wave, dof);
+  if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
+
+  // ---- online softmax (exp2 domain) ----
+  // Probabilities are taken against a per-row reference m instead of the
+  // exact running max: exact all the same, since output and row sum share
+  // the reference.  The reference only has to keep exp2 in range, so the
+  // row max is computed only when a lane's partial row sum leaves
+  // [0, 2^20] (some p > 2^15) or the row has no reference yet; then rows
+  // whose max exceeds m by more than 2^8 move m to it, rescale their
+  // accumulators and recompute p.  In steady state a step costs no max
+  // and no rescale.
+  uint32_t pw[16];
+  float rs = exp_half(s0, s1, c2, st.m == kNegInf ? 0.f : st.m, pw);
+  if (__builtin_amdgcn_ballot_w64(st.m == kNegInf || !(rs <= kRefSumLimit))) {
+    const float mx = row_max(s0, s1) * c2;
+    const bool grow = mx != kNegInf && (st.m == kNegInf || mx > st.m + 8.f);
+    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - mx) : 1.f;  // m = -inf: 0
+    st.m = grow ? mx : st.m;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.acc[i] *= alpha;
+    rs = exp_half(s0, s1, c2, st.m == kNegInf ? 0.f : st.m, pw);
+  }
+  st.l += rs;
+
+  // ---- O^T += V^T P^T ----
+  const char* vb = (const char*)&tl.v[0][0];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
+    const bf16x8 pop = as_bf16x8(make_uint4(pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const char* p = vb + voff[db] + ks * 16 * 2 * D;
+      const s16x4 lo = ld_tr(p), hi = ld_tr(p + 8 * 2 * D);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, st.acc[db], 0, 0, 0);
+    }
+  }
+
+  cur = nxt;
+  load_meta(a, next_blk, it.blk_end, it.q_min, nxt);
+  __syncthreads();   // waits for this wave's DMA, then for every wave
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) {
-  __shared__ PrefillSmem<D> sm;
+  __shared__ StepTile<D> tile0;
+  __shared__ StepTile<D> tile1;
   const WorkItem it = a.items[blockIdx.x];
   const int t = threadIdx.x;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int h = lane >> 5;        // lane half: which 8 of each 16 reduction indices
   const int col = lane & 31;      // tile row within the wave
   const int mrow = wave * 32 + col;
   const RowInfo ri = row_info(a, it, mrow);
 
-  // Q^T operand: lane holds q[row][16ks + 8h .. +8) for every ks.
-  bf16x8 qop[D / 16];
+  TileState<D> st;
   {
+    // Q^T operand: lane holds q[row][16ks + 8h .. +8) for every ks.
     const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)ri.token * a.num_q_heads + ri.head) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qop[ks] = as_bf16x8(ri.ok ? *(const uint4*)(qrow + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0));
+      st.qop[ks] = as_bf16x8(ri.ok ? *(const uint4*)(qrow + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0));
   }
-
-  f32x16 acc[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){0};
-  float m = kNegInf, l = 0.f;
-  const float c2 = a.scale_log2;
+  for (int i = 0; i < D / 32; ++i) st.acc[i] = (f32x16){0};
+  st.m = kNegInf;
+  st.l = 0.f;
 
   const int nblk = it.blk_end - it.blk_begin;
   const int nsteps = (nblk + 3) >> 2;
   if (nsteps > 0) {
+    const DmaOffsets<D> dof = dma_offsets<D>(lane);
+    uint32_t voff[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) voff[db] = vtr_offset<D>(lane, db);
     StepMeta cur, nxt;
-    StepRegs<D> regs;
     load_meta(a, it.blk_begin, it.blk_end, it.q_min, cur);
-    fetch_k<D>(a, it.kv_head, cur, regs, t);
-    fetch_v<D>(a, it.kv_head, cur, regs, t);
-    stage_k<D>(sm, 0, regs, t);
-    stage_v<D>(sm, 0, regs, cur, t);
+    dma_step<D>(a, it.kv_head, cur, tile0, wave, dof);
     load_meta(a, it.blk_begin + 4, it.blk_end, it.q_min, nxt);
     __syncthreads();
 
-    for (int s = 0; s < nsteps; ++s) {
-      const int buf = s & 1;
-      // Next step's K (a step past the item's end reads in-bounds pool blocks
-      // and is never used).
-      fetch_k<D>(a, it.kv_head, nxt, regs, t);
-
-      // ---- S^T = K Q^T for 64 keys ----
-      f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 k0 = ld_k<D>(sm, buf, col, 2 * ks + h);
-        const bf16x8 k1 = ld_k<D>(sm, buf, 32 + col, 2 * ks + h);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[ks], s1, 0, 0, 0);
-      }
-      stage_k<D>(sm, buf ^ 1, regs, t);
-      fetch_v<D>(a, it.kv_head, nxt, regs, t);
-
-      if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
-
-      // ---- online softmax (exp2 domain) ----
-      // Probabilities are taken against a per-row reference m instead of the
-      // exact running max: exact all the same, since output and row sum share
-      // the reference.  The reference only has to keep exp2 in range, so the
-      // row max is computed only when a lane's partial row sum leaves
-      // [0, 2^20] (some p > 2^15) or the row has no reference yet; then rows
-      // whose max exceeds m by more than 2^8 move m to it, rescale their
-      // accumulators and recompute p.  In steady state a step costs no max
-      // and no rescale.
-      uint32_t pw[16];
-      float rs = exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
-      if (__builtin_amdgcn_ballot_w64(m == kNegInf || !(rs <= kRefSumLimit))) {
-        const float mx = row_max(s0, s1) * c2;
-        const bool grow = mx != kNegInf && (m == kNegInf || mx > m + 8.f);
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;  // m = -inf: 0
-        m = grow ? mx : m;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-        rs = exp_half(s0, s1, c2, m == kNegInf ? 0.f : m, pw);
-      }
-      l += rs;
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int w0 = (ks >> 1) * 8 + (ks & 1) * 4;
-        const bf16x8 pop = as_bf16x8(make_uint4(pw[w0], pw[w0 + 1], pw[w0 + 2], pw[w0 + 3]));
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 v = ld_vt<D>(sm, buf, db * 32 + col, 2 * ks + h);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, acc[db], 0, 0, 0);
-        }
-      }
-
-      stage_v<D>(sm, buf ^ 1, regs, nxt, t);
-      cur = nxt;
-      load_meta(a, it.blk_begin + 4 * (s + 2), it.blk_end, it.q_min, nxt);
-      __syncthreads();
+    // Unrolled by two so that each step's tiles are known at compile time.
+    for (int s = 0; s < nsteps; s += 2) {
+      chunk_step<D>(a, it, ri, st, tile0, tile1, cur, nxt, it.blk_begin + 4 * (s + 2), wave, lane, dof, voff);
+      if (s + 1 >= nsteps) break;
+      chunk_step<D>(a, it, ri, st, tile1, tile0, cur, nxt, it.blk_begin + 4 * (s + 3), wave, lane, dof, voff);
     }
   }
 
   // ---- epilogue ----
-  write_rows<D>(a, it, ri, mrow, h, acc, m, l + __shfl_xor(l, 32, 64));
+  write_rows<D>(a, it, ri, mrow, h, st.acc, st.m, st.l + __shfl_xor(st.l, 32, 64));
 }
 
 }  // namespace
