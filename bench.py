@@ -91,6 +91,24 @@ def percentiles(samples_ms):
     return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "n": int(len(samples_ms))}
 
 
+SETTLE_S = 0.3   # seconds of back-to-back calls before the warm-up steps
+
+
+def settle(call, seconds=SETTLE_S):
+    """Run `call` back to back until the GPU has been busy for `seconds`.
+
+    From idle the GPU needs some tens of milliseconds of load before its clocks
+    settle; without this the first timed calls of a short run come out ~12 %
+    slower than steady state (0.165 against 0.146 ms per prefill call).  The
+    timed region still holds exactly the requested steps."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            call()
+        torch.cuda.synchronize()
+
+
 def run_workload(wl, steps, warmup, kind, cold=False):
     """Time msa_forward over the workload: wall clock per call over back-to-back
     calls, then per-kernel HIP-event times (totals and per-launch samples for
@@ -107,6 +125,7 @@ def run_workload(wl, steps, warmup, kind, cold=False):
     bt = torch.from_numpy(wl.block_table).cuda()
     desc = msa.SegDesc.from_workload(wl)
     stream = torch.cuda.current_stream()
+    settle(lambda: msa.forward(q, desc, bt, pool, out, lse, stream))
     for _ in range(warmup):
         msa.forward(q, desc, bt, pool, out, lse, stream)
     torch.cuda.synchronize()
@@ -167,6 +186,7 @@ def run_write(wl, fresh, steps, warmup):
     bt = torch.from_numpy(wl.block_table).cuda()
     flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    settle(lambda: msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream))
     for _ in range(warmup):
         msa.write_kv(pool, ks, vs, fresh.segs, fresh.src_rows, bt, stream)
     torch.cuda.synchronize()
@@ -484,7 +504,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "settle_s": SETTLE_S,
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": 16, "total_q": wl.total_q,
                    "segments": int(len(wl.segs)), "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
