@@ -48,7 +48,8 @@ def oracle_result(wl, rows=None):
 def compare(wl, out, lse, ref_out, ref_lse, rows=None):
     """Assert the GPU result matches the oracle within the dtype's bound.
 
-    Returns (max_abs, mean_abs) of the output error."""
+    Returns (max_abs, mean_abs) of the output error; the lse margins of the
+    last call are left in ``compare.last`` (a dict of all four figures)."""
     if rows is None:
         rows = np.arange(wl.total_q)
     rows = np.asarray(rows)
@@ -71,7 +72,10 @@ def compare(wl, out, lse, ref_out, ref_lse, rows=None):
         assert lerr.max(initial=0) <= BF16_MAX_ABS, lerr.max()
         if lerr.size:
             assert lerr.mean() <= BF16_MEAN_ABS, lerr.mean()
-    return float(err.max(initial=0)), float(err.mean()) if err.size else 0.0
+    compare.last = {"rows": int(len(rows)),
+                    "out_max_abs": float(err.max(initial=0)), "out_mean_abs": float(err.mean()) if err.size else 0.0,
+                    "lse_max_abs": float(lerr.max(initial=0)), "lse_mean_abs": float(lerr.mean()) if lerr.size else 0.0}
+    return compare.last["out_max_abs"], compare.last["out_mean_abs"]
 
 
 def sample_rows(wl, n, seed):
