@@ -135,6 +135,32 @@ typedef struct {
 int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_table,
                 msa_pool* pool, void* out, float* lse, void* stream);
 
+/* ---- attention without allocation --------------------------------------------- */
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and checks as msa_forward, with the same kernels,
+ * but the call's plan and the partial results of split work go to a fixed
+ * scratch array that the library holds on each GPU it runs on (16 MiB per
+ * GPU, kept until the process ends) instead of the pool's workspace.  The call
+ * makes no hipMalloc, hipFree, pinned or other device allocation; its plan
+ * goes from host memory of the calling thread into the scratch through
+ * hipMemcpyAsync on `stream` (a copy from pageable memory, so the call waits
+ * until the host side of that copy has been taken).  No kernel timing is
+ * recorded (MSA_OPT_TIMING is ignored); MSA_OPT_SPLIT_BLOCKS and
+ * MSA_OPT_NUM_CUS apply.
+ *
+ * Limits: at most 2 MiB of packed plan (block list of 8 bytes per KV block,
+ * 4 bytes per query row, 32 bytes per work item, each part rounded to 256
+ * bytes) and 12 MiB of split partials ((head_dim + 1) * 4 bytes per partial
+ * row); a call beyond either returns MSA_ERR_WORKSPACE before any HIP call.
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * contents (each call writes all it reads); calls on one GPU whose work can
+ * overlap -- on different streams, or from different host threads -- race on
+ * it, so the caller must order them.
+ * Errors: as msa_forward, plus WORKSPACE for the limits above. */
+int msa_forward_noalloc(const void* q, const msa_seg_desc* desc, const int32_t* block_table,
+                        msa_pool* pool, void* out, float* lse, void* stream);
+
 /* ---- KV write (recompute-scatter) ------------------------------------------- */
 /* Place freshly computed K/V rows -- a prefill chunk's own tokens, or evicted
  * blocks rebuilt on demand (abstract and section 4.1 / Figure 5 of the

@@ -15,7 +15,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "MsaError", "Pool", "SegDesc", "forward", "write_kv", "plan_debug", "library_path", "load_library",
+    "MsaError", "Pool", "SegDesc", "forward", "forward_noalloc", "write_kv", "plan_debug", "library_path", "load_library",
     "LatencyModel", "latency_fit", "chunk_blocks",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
@@ -30,7 +30,8 @@ OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS = 1, 2, 3
 KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_WRITE = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
-    "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_write_kv", "msa_last_error",
+    "msa_create_pool", "msa_pool_kv_ptrs", "msa_destroy_pool", "msa_forward", "msa_forward_noalloc",
+    "msa_write_kv", "msa_last_error",
     "msa_pool_set_option", "msa_pool_kernel_time", "msa_pool_kernel_samples", "msa_plan_debug",
     "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b", "msa_chunk_blocks",
 )
@@ -90,6 +91,7 @@ def load_library():
     lib.msa_pool_kv_ptrs.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P)]
     lib.msa_destroy_pool.argtypes = [P]
     lib.msa_forward.argtypes = [P, ctypes.POINTER(_SegDesc), P, P, P, P, P]
+    lib.msa_forward_noalloc.argtypes = [P, ctypes.POINTER(_SegDesc), P, P, P, P, P]
     lib.msa_write_kv.argtypes = [P, P, P, I32, P, P, I32, P, I32, P]
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
@@ -225,6 +227,15 @@ def forward(q, seg_desc: SegDesc, block_table, pool: Pool, out, lse=None, stream
     _check_forward_tensors(q, seg_desc, block_table, pool, out, lse)
     _check(load_library().msa_forward(_ptr(q), ctypes.byref(seg_desc.c), _ptr(block_table), pool.handle,
                                       _ptr(out), _ptr(lse), _current_stream(stream)))
+
+
+def forward_noalloc(q, seg_desc: SegDesc, block_table, pool: Pool, out, lse=None, stream=None):
+    """As ``forward``, through msa_forward_noalloc: the call allocates no device
+    memory (its plan and split partials live in the library's fixed per-GPU
+    scratch; calls on one GPU must not overlap)."""
+    _check_forward_tensors(q, seg_desc, block_table, pool, out, lse)
+    _check(load_library().msa_forward_noalloc(_ptr(q), ctypes.byref(seg_desc.c), _ptr(block_table), pool.handle,
+                                              _ptr(out), _ptr(lse), _current_stream(stream)))
 
 
 def _is_tensor(x) -> bool:

@@ -258,6 +258,144 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
+// ---- one attention call: checks, plan layout, packing and launches ----------
+
+// Argument checks and planning, shared by both attention entry points.  No
+// HIP call is made; *empty is set when there is nothing to enqueue.
+int prepare_call(msa_pool* p, const msa_seg_desc* desc, const void* q, const int32_t* block_table, const void* out,
+                 const float* lse, bool* empty) {
+  if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
+  if (!desc) return set_error(MSA_ERR_INVALID_ARG, "seg_desc is NULL");
+  PlanConfig cfg;
+  cfg.num_kv_heads = p->desc.num_kv_heads;
+  cfg.head_dim = p->desc.head_dim;
+  cfg.dtype = p->desc.dtype;
+  cfg.num_cus = p->num_cus_override > 0 ? p->num_cus_override : (p->num_cus > 0 ? p->num_cus : 256);
+  cfg.split_blocks = p->split_blocks;
+  std::string err;
+  int rc = build_plan(desc, cfg, p->plan, err);
+  if (rc) return set_error(rc, "%s", err.c_str());
+  const Plan& plan = p->plan;
+  if (plan.total_q > 0 && (!q || !out)) return set_error(MSA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!plan.blocks.empty() && !block_table) return set_error(MSA_ERR_INVALID_ARG, "block_table is NULL");
+  if (plan.total_q > 0 && (q == out || (const void*)lse == q || (const void*)lse == out))
+    return set_error(MSA_ERR_INVALID_ARG, "q, out and lse must not alias");
+  *empty = plan.total_q == 0;
+  return MSA_OK;
+}
+
+// On the first call, learn the device's compute-unit count and plan again if
+// it differs from the count assumed.  The device must be current.
+int refresh_cus(msa_pool* p, const msa_seg_desc* desc) {
+  if (p->num_cus != 0) return MSA_OK;
+  int n = 0;
+  MSA_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, p->desc.device));
+  const int assumed = p->num_cus_override > 0 ? p->num_cus_override : 256;
+  p->num_cus = n > 0 ? n : 256;
+  if (p->num_cus_override == 0 && p->num_cus != assumed) {
+    PlanConfig cfg;
+    cfg.num_kv_heads = p->desc.num_kv_heads;
+    cfg.head_dim = p->desc.head_dim;
+    cfg.dtype = p->desc.dtype;
+    cfg.num_cus = p->num_cus;
+    cfg.split_blocks = p->split_blocks;
+    std::string err;
+    int rc = build_plan(desc, cfg, p->plan, err);
+    if (rc) return set_error(rc, "%s", err.c_str());
+  }
+  return MSA_OK;
+}
+
+// Where each part of a call's plan sits in the packed plan buffer, and the
+// size of its partial-result area.
+struct PlanLayout {
+  size_t off_blocks, off_qpos, off_items[3], off_merge, plan_bytes;
+  size_t off_part_lse, part_bytes;
+};
+
+// The block list is followed by kBlockPad zero entries so that a kernel may
+// always read the entries of a step (their valid counts are ignored).
+constexpr size_t kBlockPad = 4;
+
+PlanLayout plan_layout(const Plan& plan, int D) {
+  PlanLayout L{};
+  size_t off = 0;
+  L.off_blocks = off;
+  off = align_up(off + (plan.blocks.size() + kBlockPad) * sizeof(BlockEntry), 256);
+  L.off_qpos = off;
+  off = align_up(off + plan.q_pos.size() * sizeof(int32_t), 256);
+  for (int k = 0; k < 3; ++k) {
+    L.off_items[k] = off;
+    off = align_up(off + plan.items[k].size() * sizeof(WorkItem), 256);
+  }
+  L.off_merge = off;
+  off = align_up(off + plan.merges.size() * sizeof(MergeItem), 256);
+  L.plan_bytes = off;
+  L.off_part_lse = align_up((size_t)plan.part_rows * D * sizeof(float), 256);
+  L.part_bytes = plan.part_rows > 0 ? L.off_part_lse + align_up((size_t)plan.part_rows * sizeof(float), 256) : 0;
+  return L;
+}
+
+void pack_plan(const Plan& plan, const PlanLayout& L, char* h) {
+  if (!plan.blocks.empty()) memcpy(h + L.off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
+  memset(h + L.off_blocks + plan.blocks.size() * sizeof(BlockEntry), 0, kBlockPad * sizeof(BlockEntry));
+  memcpy(h + L.off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
+  for (int k = 0; k < 3; ++k)
+    if (!plan.items[k].empty())
+      memcpy(h + L.off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
+  if (!plan.merges.empty()) memcpy(h + L.off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
+}
+
+// Enqueue the attention kernels of a planned call whose plan is in device
+// memory at `dplan` (block ids resolved) and whose partials go to `dpart`.
+int launch_attention(msa_pool* p, const msa_seg_desc* desc, const PlanLayout& L, char* dplan, char* dpart,
+                     const void* q, void* out, float* lse, hipStream_t stream, bool timed) {
+  const Plan& plan = p->plan;
+  const int D = p->desc.head_dim;
+  KernelArgs a{};
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.k = p->k;
+  a.v = p->v;
+  a.blocks = (const BlockEntry*)(dplan + L.off_blocks);
+  a.q_pos = (const int32_t*)(dplan + L.off_qpos);
+  a.merges = (const MergeItem*)(dplan + L.off_merge);
+  a.n_merges = (int32_t)plan.merges.size();
+  a.part_o = (float*)dpart;
+  a.part_lse = dpart ? (float*)(dpart + L.off_part_lse) : nullptr;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = p->desc.num_kv_heads;
+  a.group = desc->num_q_heads / p->desc.num_kv_heads;
+  a.causal = desc->causal;
+  const float scale = desc->scale != 0.f ? desc->scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  auto launch = [&](int kind, auto&& fn) -> int {
+    if (timed) return timed_launch(p, kind, stream, fn);
+    const int e = fn();
+    return e != hipSuccess ? hip_error((hipError_t)e, "kernel launch") : MSA_OK;
+  };
+  for (int k = 0; k < 3; ++k) {
+    if (plan.items[k].empty()) continue;
+    a.items = (const WorkItem*)(dplan + L.off_items[k]);
+    a.n_items = (int32_t)plan.items[k].size();
+    a.max_mrows = plan.max_mrows[k];
+    const int rc = launch(k, [&]() {
+      if (k == kPrefill) return launch_prefill(a, D, stream);
+      if (k == kDecode) return launch_decode(a, D, stream);
+      return launch_fp32(a, D, stream);
+    });
+    if (rc) return rc;
+  }
+  if (!plan.merges.empty()) {
+    a.items = nullptr;
+    a.n_items = 0;
+    const int rc = launch(kMerge, [&]() { return launch_merge(a, D, p->desc.dtype, stream); });
+    if (rc) return rc;
+  }
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -429,116 +567,68 @@ int msa_plan_debug(const msa_seg_desc* desc, int32_t num_kv_heads, int32_t head_
 
 int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_table, msa_pool* p,
                 void* out, float* lse, void* stream_) {
-  // ---- host-side checks and planning (no HIP call before they pass) ----
-  if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
-  if (!desc) return set_error(MSA_ERR_INVALID_ARG, "seg_desc is NULL");
-  PlanConfig cfg;
-  cfg.num_kv_heads = p->desc.num_kv_heads;
-  cfg.head_dim = p->desc.head_dim;
-  cfg.dtype = p->desc.dtype;
-  cfg.num_cus = p->num_cus_override > 0 ? p->num_cus_override : (p->num_cus > 0 ? p->num_cus : 256);
-  cfg.split_blocks = p->split_blocks;
-  std::string err;
-  int rc = build_plan(desc, cfg, p->plan, err);
-  if (rc) return set_error(rc, "%s", err.c_str());
-  Plan& plan = p->plan;
-  if (plan.total_q > 0 && (!q || !out)) return set_error(MSA_ERR_INVALID_ARG, "q or out is NULL");
-  if (!plan.blocks.empty() && !block_table) return set_error(MSA_ERR_INVALID_ARG, "block_table is NULL");
-  if (plan.total_q > 0 && (q == out || (const void*)lse == q || (void*)lse == out))
-    return set_error(MSA_ERR_INVALID_ARG, "q, out and lse must not alias");
-  if (plan.total_q == 0) return MSA_OK;
-
+  bool empty = false;
+  int rc = prepare_call(p, desc, q, block_table, out, lse, &empty);
+  if (rc || empty) return rc;
   hipStream_t stream = (hipStream_t)stream_;
   DeviceGuard guard(p->desc.device);
   if (!guard.ok) return set_error(MSA_ERR_HIP, "cannot select device %d", p->desc.device);
-  if (p->num_cus == 0) {
-    int n = 0;
-    MSA_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, p->desc.device));
-    p->num_cus = n > 0 ? n : 256;
-    if (p->num_cus_override == 0 && p->num_cus != cfg.num_cus) {
-      cfg.num_cus = p->num_cus;
-      rc = build_plan(desc, cfg, plan, err);
-      if (rc) return set_error(rc, "%s", err.c_str());
-    }
-  }
-
-  // ---- pack the plan ----
-  const int D = p->desc.head_dim;
-  size_t off = 0;
-  // The block list is followed by kBlockPad zero entries so that a kernel may
-  // always read the entries of a step (their valid counts are ignored).
-  constexpr size_t kBlockPad = 4;
-  const size_t off_blocks = off;
-  off = align_up(off + (plan.blocks.size() + kBlockPad) * sizeof(BlockEntry), 256);
-  const size_t off_qpos = off;
-  off = align_up(off + plan.q_pos.size() * sizeof(int32_t), 256);
-  size_t off_items[3];
-  for (int k = 0; k < 3; ++k) {
-    off_items[k] = off;
-    off = align_up(off + plan.items[k].size() * sizeof(WorkItem), 256);
-  }
-  const size_t off_merge = off;
-  off = align_up(off + plan.merges.size() * sizeof(MergeItem), 256);
-  const size_t plan_bytes = off;
-  const size_t off_part_lse = align_up((size_t)plan.part_rows * D * sizeof(float), 256);
-  const size_t part_need = off_part_lse + align_up((size_t)plan.part_rows * sizeof(float), 256);
-
-  if (part_need > 0) {
-    rc = ensure_device(p, &p->d_part, &p->part_bytes, part_need, stream, "partial-result buffer");
-    if (rc) return rc;
-  }
-  rc = stage_and_upload(p, stream, plan_bytes, (int32_t)plan.blocks.size(), block_table, [&](char* h) {
-    if (!plan.blocks.empty()) memcpy(h + off_blocks, plan.blocks.data(), plan.blocks.size() * sizeof(BlockEntry));
-    memset(h + off_blocks + plan.blocks.size() * sizeof(BlockEntry), 0, kBlockPad * sizeof(BlockEntry));
-    memcpy(h + off_qpos, plan.q_pos.data(), plan.q_pos.size() * sizeof(int32_t));
-    for (int k = 0; k < 3; ++k)
-      if (!plan.items[k].empty())
-        memcpy(h + off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
-    if (!plan.merges.empty()) memcpy(h + off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
-  });
+  rc = refresh_cus(p, desc);
   if (rc) return rc;
-  char* dws = (char*)p->d_plan;
 
-  // ---- launches ----
-  KernelArgs a{};
-  a.q = q;
-  a.out = out;
-  a.lse = lse;
-  a.k = p->k;
-  a.v = p->v;
-  a.block_table = block_table;
-  a.blocks = (const BlockEntry*)(dws + off_blocks);
-  a.q_pos = (const int32_t*)(dws + off_qpos);
-  a.merges = (const MergeItem*)(dws + off_merge);
-  a.n_merges = (int32_t)plan.merges.size();
-  a.part_o = (float*)p->d_part;
-  a.part_lse = (float*)((char*)p->d_part + off_part_lse);
-  a.num_q_heads = desc->num_q_heads;
-  a.num_kv_heads = p->desc.num_kv_heads;
-  a.group = desc->num_q_heads / p->desc.num_kv_heads;
-  a.causal = desc->causal;
-  const float scale = desc->scale != 0.f ? desc->scale : 1.0f / std::sqrt((float)D);
-  a.scale_log2 = scale * 1.4426950408889634f;
-
-  for (int k = 0; k < 3; ++k) {
-    if (plan.items[k].empty()) continue;
-    a.items = (const WorkItem*)(dws + off_items[k]);
-    a.n_items = (int32_t)plan.items[k].size();
-    a.max_mrows = plan.max_mrows[k];
-    rc = timed_launch(p, k, stream, [&]() {
-      if (k == kPrefill) return launch_prefill(a, D, stream);
-      if (k == kDecode) return launch_decode(a, D, stream);
-      return launch_fp32(a, D, stream);
-    });
+  const Plan& plan = p->plan;
+  const PlanLayout L = plan_layout(plan, p->desc.head_dim);
+  if (L.part_bytes > 0) {
+    rc = ensure_device(p, &p->d_part, &p->part_bytes, L.part_bytes, stream, "partial-result buffer");
     if (rc) return rc;
   }
-  if (!plan.merges.empty()) {
-    a.items = nullptr;
-    a.n_items = 0;
-    rc = timed_launch(p, kMerge, stream, [&]() { return launch_merge(a, D, p->desc.dtype, stream); });
-    if (rc) return rc;
+  rc = stage_and_upload(p, stream, L.plan_bytes, (int32_t)plan.blocks.size(), block_table,
+                        [&](char* h) { pack_plan(plan, L, h); });
+  if (rc) return rc;
+  return launch_attention(p, desc, L, (char*)p->d_plan, (char*)p->d_part, q, out, lse, stream, p->timing);
+}
+
+int msa_forward_noalloc(const void* q, const msa_seg_desc* desc, const int32_t* block_table, msa_pool* p,
+                        void* out, float* lse, void* stream_) {
+  bool empty = false;
+  int rc = prepare_call(p, desc, q, block_table, out, lse, &empty);
+  if (rc || empty) return rc;
+  {
+    const PlanLayout L = plan_layout(p->plan, p->desc.head_dim);
+    if (L.plan_bytes > kScratchPlanBytes || L.part_bytes > kScratchPartBytes)
+      return set_error(MSA_ERR_WORKSPACE,
+                       "call needs %zu plan bytes and %zu partial-result bytes; the fixed scratch holds at most "
+                       "%zu and %zu",
+                       L.plan_bytes, L.part_bytes, kScratchPlanBytes, kScratchPartBytes);
   }
-  return MSA_OK;
+  hipStream_t stream = (hipStream_t)stream_;
+  DeviceGuard guard(p->desc.device);
+  if (!guard.ok) return set_error(MSA_ERR_HIP, "cannot select device %d", p->desc.device);
+  rc = refresh_cus(p, desc);
+  if (rc) return rc;
+  const Plan& plan = p->plan;
+  const PlanLayout L = plan_layout(plan, p->desc.head_dim);
+  if (L.plan_bytes > kScratchPlanBytes || L.part_bytes > kScratchPartBytes)
+    return set_error(MSA_ERR_WORKSPACE, "plan for %d compute units exceeds the fixed scratch", p->num_cus);
+  void* base = nullptr;
+  std::string err;
+  rc = scratch_address(p->desc.device, &base, err);
+  if (rc) return set_error(rc, "%s", err.c_str());
+  char* stage = (char*)base;                       // host copy of the packed plan
+  char* dplan = stage + kScratchPlanBytes;          // the plan the kernels read
+  char* dpart = dplan + kScratchPlanBytes;          // split partials
+
+  // Pack into host memory of this thread and copy it into the scratch on the
+  // stream.  A copy from pageable memory returns once its source has been
+  // taken, so the host buffer is free again when the call returns.
+  thread_local std::vector<char> host;
+  if (host.size() < L.plan_bytes) host.resize(L.plan_bytes);
+  pack_plan(plan, L, host.data());
+  MSA_HIP(hipMemcpyAsync(stage, host.data(), L.plan_bytes, hipMemcpyHostToDevice, stream));
+  int e = launch_upload(stage, dplan, L.plan_bytes, (int32_t)plan.blocks.size(), block_table, p->desc.num_blocks,
+                        stream);
+  if (e != hipSuccess) return hip_error((hipError_t)e, "kernel launch");
+  return launch_attention(p, desc, L, dplan, dpart, q, out, lse, stream, false);
 }
 
 int msa_write_kv(msa_pool* p, const void* k_src, const void* v_src, int32_t num_src_rows, const msa_segment* segs,

@@ -18,6 +18,13 @@ constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accept
 constexpr int kBtIndexBits = 28;     // index bits in BlockEntry::bt_valid
 constexpr int kMaxPoolBlocks = 1 << kBtIndexBits;
 
+// Fixed device scratch of msa_forward_noalloc (one copy per GPU): the host
+// copy of a call's packed plan, the plan as the kernels read it (block ids
+// resolved), then the partial results of split tiles.
+constexpr size_t kScratchPlanBytes = size_t(2) << 20;
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchPartBytes = kScratchBytes - 2 * kScratchPlanBytes;
+
 // One entry of a sequence's position-ordered block list (8 bytes).  The host
 // writes the block-table index; the upload kernel replaces it, on the device,
 // by the pool block id it names, so kernels never chase block_table.
@@ -113,6 +120,11 @@ struct WriteArgs {
   int32_t n_entries;
   int32_t num_kv_heads;
 };
+
+// Device address of this GPU's copy of the fixed scratch (kScratchBytes),
+// looked up once per device with that device current.  Returns an MSA_*
+// status and fills `err` on failure.
+int scratch_address(int device, void** ptr, std::string& err);
 
 // Launchers (one per kernel source).  Return a hipError_t value.
 int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
