@@ -4,13 +4,20 @@
 
 One step is one msa_forward call over the whole workload: host planning, the
 plan upload and every kernel (chunk/prefill, decode, merge), with q, the K/V
-pool and the block table already resident in HBM.  The default workload is
+pool and the block table already resident in HBM.  The headline workload is
 chunked prefill (4 sequences, GQA 32/8, head_dim 128, 4096-token context in 6
 scattered segments plus a 512-token chunk), reported in TFLOP/s of visible
-(query, key) pairs; the decode workload (64 sequences, 1k-8k-token contexts in
-2-16 segments over a 2M-token pool) is reported alongside in GB/s, and so is
-the KV write (msa_write_kv) of the mixed batch's fresh rows (16 sequences,
-61 fresh segments, 44 820 rows of 8 kv heads x 128) into its 65 536-block pool.
+(query, key) pairs.  Reported alongside, each against its roofline:
+  * decode (64 sequences, 1k-8k-token contexts in 2-16 segments over a
+    2M-token pool), HBM GB/s;
+  * heavy fragmentation (2 sequences, 32 768-token contexts in 64 segments
+    with position gaps, 2048-token chunks), TFLOP/s;
+  * the mixed batch (16 sequences, GQA 64/8: 8 prefill chunks and 8 decode
+    tokens over 2k-16k-token contexts), whole batch as T_roof / T, and its
+    prefill-only and decode-only parts separately;
+  * the tiny fp32 case (time only);
+  * the KV write (msa_write_kv) of the mixed batch's fresh rows (61 fresh
+    segments, 44 820 rows of 8 kv heads x 128) into its 65 536-block pool.
 
 Prints one JSON line.
 """
@@ -23,6 +30,33 @@ import os
 import sys
 import time
 
+
+def _blas_threads() -> int:
+    """Threads for the CPU baseline's BLAS: the CPUs this process may run on,
+    capped by an OMP_NUM_THREADS the environment already sets.  Set before
+    numpy is first imported, so that OpenBLAS/MKL/OpenMP pick it up."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, str(n))
+    return n
+
+
+BLAS_THREADS = _blas_threads()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -32,6 +66,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"prefill": "kv_cache_attention_msa_amd/csrc/msa_prefill.hip",
                   "decode": "kv_cache_attention_msa_amd/csrc/msa_decode.hip",
                   "write": "kv_cache_attention_msa_amd/csrc/msa_write.hip"}
+GATE_MFMA, GATE_HBM = 0.60, 0.70     # roofline fractions the benchmark definition asks for
 
 
 def visible_counts(wl):
@@ -70,10 +105,14 @@ def source_sha(rel):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else None
 
 
+def traffic_path(kernel, units):
+    return os.path.join(ROOT, "profiles", f"{kernel}_traffic_{units}.json")
+
+
 def traffic_for(kernel, units):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if the
     kernel source still matches the one the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    path = traffic_path(kernel, units)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -109,16 +148,17 @@ def settle(call, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
-def run_workload(wl, steps, warmup, kind, cold=False):
+def run_workload(wl, steps, warmup, kind, cold=False, pool_kv=None):
     """Time msa_forward over the workload: wall clock per call over back-to-back
     calls, then per-kernel HIP-event times (totals and per-launch samples for
     `kind`); with cold, also `kind`'s launch times when a 1 GiB read between
-    calls has evicted the Infinity Cache."""
+    calls has evicted the Infinity Cache.  pool_kv: resident (K, V) to reuse."""
     import torch
     import kv_cache_attention_msa_amd as msa
 
-    K, V = wl.dense_pool("cuda")
-    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K, v=V)
+    K, V = pool_kv if pool_kv is not None else wl.dense_pool("cuda")
+    dt = msa.FP32 if wl.dtype == "fp32" else msa.BF16
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, dt, k=K, v=V)
     q = wl.q.cuda()
     out = torch.empty_like(q)
     lse = torch.empty(wl.total_q, wl.num_q_heads, dtype=torch.float32, device="cuda")
@@ -140,7 +180,8 @@ def run_workload(wl, steps, warmup, kind, cold=False):
     for _ in range(steps):
         msa.forward(q, desc, bt, pool, out, lse, stream)
     torch.cuda.synchronize()
-    times = {k: pool.kernel_time(k) for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE, msa.KERNEL_MERGE)}
+    times = {k: pool.kernel_time(k) for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE, msa.KERNEL_FP32,
+                                              msa.KERNEL_MERGE, msa.KERNEL_UPLOAD)}
     times["dist"] = percentiles(pool.kernel_samples(kind))
     if cold:
         flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
@@ -165,11 +206,12 @@ def run_workload(wl, steps, warmup, kind, cold=False):
     plan_ms = sorted(host)[len(host) // 2] * 1e3
     pool.close()
     del K, V
-    torch.cuda.empty_cache()
+    if pool_kv is None:
+        torch.cuda.empty_cache()
     return wall / steps * 1e3, times, plan_ms
 
 
-def run_write(wl, fresh, steps, warmup):
+def run_write(wl, fresh, steps, warmup, pool_kv=None):
     """Time msa_write_kv of the workload's fresh rows into its pool.
 
     Returns (wall ms per call, warm kernel ms, cold kernel ms, launches): wall
@@ -180,7 +222,7 @@ def run_write(wl, fresh, steps, warmup):
     import torch
     import kv_cache_attention_msa_amd as msa
 
-    K, V = wl.dense_pool("cuda")
+    K, V = pool_kv if pool_kv is not None else wl.dense_pool("cuda")
     pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K, v=V)
     ks, vs = fresh.k.cuda(), fresh.v.cuda()
     bt = torch.from_numpy(wl.block_table).cuda()
@@ -267,8 +309,10 @@ def cpu_baseline(wl, flops_per_row, budget_s=12.0):
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": done_flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{seqs} of {wl.batch} sequences ({done_rows} query rows x {wl.num_q_heads} heads, "
-                      f"all their visible keys), fp64 numpy, {t:.1f} s"}
+            "sample": f"{seqs} of {wl.batch} sequences of {wl.name} ({done_rows} query rows x {wl.num_q_heads} "
+                      f"heads, all their visible keys), fp64 numpy, {t:.1f} s",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads_requested": BLAS_THREADS}
 
 
 # ---------------------------------------------------------------------------
@@ -335,7 +379,7 @@ def write_report(args):
                   f"- scaled traffic per launch: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written "
                   f"= {(fetch_b + write_b) / 1e6:.1f} MB",
                   f"- kernel source sha256[:16]: {rec['kernel_src_sha']}"]
-        with open(os.path.join(ROOT, "profiles", f"{args.key}_traffic.json"), "w") as fh:
+        with open(traffic_path(args.key, args.units), "w") as fh:
             json.dump(rec, fh, indent=1)
     if args.notes:
         lines += ["", "## Notes", ""] + [f"- {n}" for n in args.notes]
@@ -423,7 +467,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "write"], help="time one workload only (profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "write", "heavy", "mixed", "mixed_prefill", "mixed_decode",
+                                       "tiny"], help="time one workload only (profiler runs)")
     ap.add_argument("--copy-bytes", type=int, help="run a plain copy kernel of this size (counter calibration)")
     ap.add_argument("--report", help="write a profile summary from rocprofv3 CSV output (no GPU needed)")
     ap.add_argument("--key", choices=["prefill", "decode", "write"])
@@ -470,15 +515,21 @@ def main():
     if args.only:
         import kv_cache_attention_msa_amd as msa
         import workloads as W
-        wl = W.config2() if args.only == "prefill" else W.config3()
-        kind = msa.KERNEL_PREFILL if args.only == "prefill" else msa.KERNEL_DECODE
+        if args.only in ("mixed", "mixed_prefill", "mixed_decode"):
+            wl = W.config5()
+            pre, dec = W.mixed_parts(wl)
+            if args.only != "mixed":
+                wl = W.subset(wl, pre if args.only == "mixed_prefill" else dec, wl.name + "_" + args.only[6:] + "_part")
+        else:
+            wl = {"prefill": W.config2, "decode": W.config3, "heavy": W.config4, "tiny": W.config1}[args.only]()
+        kind = {"decode": msa.KERNEL_DECODE, "mixed_decode": msa.KERNEL_DECODE,
+                "tiny": msa.KERNEL_FP32}.get(args.only, msa.KERNEL_PREFILL)
         ms, times, plan_ms = run_workload(wl, args.steps, args.warmup, kind)
         k_ms, k_n = times[kind]
         print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_avg_ms": k_ms / max(k_n, 1),
                           "launches": k_n}), flush=True)
         return
 
-    import numpy as np
     import torch
     import kv_cache_attention_msa_amd as msa
     import workloads as W
@@ -489,20 +540,9 @@ def main():
     flops, nbytes = work_of(wl)
     counts, _ = visible_counts(wl)
     ms, times, plan_ms = run_workload(wl, args.steps, args.warmup, msa.KERNEL_PREFILL)
-    pre_ms, pre_n = times[msa.KERNEL_PREFILL]
-    dec_ms, dec_n = times[msa.KERNEL_DECODE]
-    mrg_ms, mrg_n = times[msa.KERNEL_MERGE]
-    value = flops / (ms * 1e-3) / 1e12
-    # dominant kernel: the chunk (prefill) kernel; one launch processes the whole workload
-    k_avg = pre_ms / max(pre_n, 1)
-    achieved = flops / (k_avg * 1e-3) / 1e12 if pre_n else None
-    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
-                "traffic": traffic_for("prefill", wl.name),
-                "kernel": "msa_prefill (bf16 MFMA)", "kernel_ms": k_avg, "kernel_ms_dist": times["dist"],
-                "merge_ms": mrg_ms / mrg_n if mrg_n else 0.0, "launches_per_step": (pre_n + dec_n + mrg_n) / args.steps}
+    roofline = mfma_roofline(wl, flops, times, args.steps)
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "settle_s": SETTLE_S,
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
@@ -512,51 +552,142 @@ def main():
         "roofline": roofline,
     }
     if not args.no_secondary:
-        wl3 = W.config3()
-        f3, b3 = work_of(wl3)
-        ms3, t3, plan3 = run_workload(wl3, args.steps, args.warmup, msa.KERNEL_DECODE, cold=True)
-        d_ms, d_n = t3[msa.KERNEL_DECODE]
-        m_ms, m_n = t3[msa.KERNEL_MERGE]
-        d_avg = d_ms / max(d_n, 1)
-        ach = b3 / (d_avg * 1e-3) / 1e9 if d_n else None
-        line["secondary"] = {
-            "workload": wl3.name, "metric": "decode HBM GB/s", "value": b3 / (ms3 * 1e-3) / 1e9, "unit": "GB/s",
-            "ms_per_step": ms3, "algorithmic_bytes": b3, "algorithmic_flops": f3, "host_call_ms": plan3,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": ach / PEAK_HBM_GBS if ach else None,
-                         "traffic": traffic_for("decode", wl3.name), "kernel": "msa_decode",
-                         "kernel_ms": d_avg, "kernel_ms_dist": t3["dist"],
-                         "kernel_ms_dist_cold": t3["cold_dist"], "merge_ms": m_ms / m_n if m_n else 0.0},
-        }
-        del wl3
-        wl5 = W.config5()
-        fresh = W.fresh_kv(wl5, seed=5)
-        b5 = write_bytes(wl5, fresh)
-        ms5, k5w, k5, n5 = run_write(wl5, fresh, args.steps, args.warmup)
-        ach5 = b5 / (k5 * 1e-3) / 1e9 if n5 else None
-        line["kv_write"] = {
-            "workload": wl5.name + "_fresh", "metric": "KV write HBM GB/s", "value": b5 / (ms5 * 1e-3) / 1e9,
-            "unit": "GB/s", "ms_per_step": ms5, "algorithmic_bytes": b5, "segments": int(len(fresh.segs)),
-            "rows": fresh.rows,
-            "roofline": {"bound": "hbm", "achieved": ach5, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": ach5 / PEAK_HBM_GBS if ach5 else None,
-                         "traffic": traffic_for("write", wl5.name + "_fresh"), "kernel": "msa_write",
-                         "kernel_ms": k5, "cache": "cold (1 GiB read between calls evicts the Infinity Cache)",
-                         "kernel_warm_ms": k5w, "achieved_warm": b5 / (k5w * 1e-3) / 1e9 if n5 else None,
-                         "kernel_ms_dist_cold": run_write.dists["cold"],
-                         "kernel_ms_dist_warm": run_write.dists["warm"]},
-        }
-        del wl5, fresh
+        line["secondary"] = decode_entry(W.config3(), args.steps, args.warmup)
+        line["heavy"] = mfma_entry(W.config4(), args.steps, args.warmup)
+        line["mixed"], line["kv_write"] = mixed_entries(W.config5(), args.steps, args.warmup)
+        line["tiny"] = tiny_entry(W.config1(), args.steps, args.warmup)
     att = attainable_peaks()
     line["attainable"] = att
-    roofline["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOPs"] if achieved else None
-    for key, ref in (("secondary", "hbm_gather_4KiB_GBps"), ("kv_write", "hbm_copy_GBps")):
-        if key in line:
-            sr = line[key]["roofline"]
-            sr["frac_of_attainable"] = sr["achieved"] / att[ref] if sr["achieved"] else None
+    for sr in rooflines(line):
+        ref = {"mfma": "mfma_bf16_TFLOPs", "hbm": "hbm_gather_4KiB_GBps", "copy": "hbm_copy_GBps"}[sr.pop("_ref")]
+        sr["frac_of_attainable"] = sr["achieved"] / att[ref] if sr.get("achieved") else None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, counts * wl.num_q_heads * 4 * wl.head_dim)
     print(json.dumps(line), flush=True)
+
+
+def rooflines(line):
+    """Every roofline object of the report (headline and sub-entries)."""
+    out = [line["roofline"]]
+    for key in ("secondary", "heavy", "kv_write"):
+        if key in line:
+            out.append(line[key]["roofline"])
+    if "mixed" in line:
+        out += [line["mixed"]["prefill_part"]["roofline"], line["mixed"]["decode_part"]["roofline"]]
+    return out
+
+
+def mfma_roofline(wl, flops, times, steps):
+    """Roofline of the chunk (MFMA) kernel: one launch processes the whole workload."""
+    import kv_cache_attention_msa_amd as msa
+    pre_ms, pre_n = times[msa.KERNEL_PREFILL]
+    dec_n = times[msa.KERNEL_DECODE][1]
+    mrg_ms, mrg_n = times[msa.KERNEL_MERGE]
+    k_avg = pre_ms / max(pre_n, 1)
+    achieved = flops / (k_avg * 1e-3) / 1e12 if pre_n else None
+    return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS if achieved else None, "gate": GATE_MFMA,
+            "traffic": traffic_for("prefill", wl.name),
+            "kernel": "msa_prefill (bf16 MFMA)", "kernel_ms": k_avg, "kernel_ms_dist": times["dist"],
+            "merge_ms": mrg_ms / mrg_n if mrg_n else 0.0, "launches_per_step": (pre_n + dec_n + mrg_n) / steps,
+            "_ref": "mfma"}
+
+
+def hbm_roofline(wl, nbytes, times, kind_key="decode"):
+    """Roofline of the decode (HBM) kernel."""
+    import kv_cache_attention_msa_amd as msa
+    d_ms, d_n = times[msa.KERNEL_DECODE]
+    m_ms, m_n = times[msa.KERNEL_MERGE]
+    d_avg = d_ms / max(d_n, 1)
+    ach = nbytes / (d_avg * 1e-3) / 1e9 if d_n else None
+    r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": ach / PEAK_HBM_GBS if ach else None, "gate": GATE_HBM,
+         "traffic": traffic_for(kind_key, wl.name), "kernel": "msa_decode",
+         "kernel_ms": d_avg, "kernel_ms_dist": times["dist"], "merge_ms": m_ms / m_n if m_n else 0.0, "_ref": "hbm"}
+    if "cold_dist" in times:
+        r["kernel_ms_dist_cold"] = times["cold_dist"]
+    return r
+
+
+def decode_entry(wl, steps, warmup):
+    import kv_cache_attention_msa_amd as msa
+    f, b = work_of(wl)
+    ms, t, plan = run_workload(wl, steps, warmup, msa.KERNEL_DECODE, cold=True)
+    return {"workload": wl.name, "metric": "decode HBM GB/s", "value": b / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "ms_per_step": ms, "algorithmic_bytes": b, "algorithmic_flops": f, "host_call_ms": plan,
+            "roofline": hbm_roofline(wl, b, t)}
+
+
+def mfma_entry(wl, steps, warmup):
+    import kv_cache_attention_msa_amd as msa
+    f, b = work_of(wl)
+    ms, t, plan = run_workload(wl, steps, warmup, msa.KERNEL_PREFILL)
+    return {"workload": wl.name, "metric": "MSA TFLOP/s", "value": f / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "ms_per_step": ms, "algorithmic_flops": f, "algorithmic_bytes": b, "host_call_ms": plan,
+            "roofline": mfma_roofline(wl, f, t, steps)}
+
+
+def mixed_entries(wl, steps, warmup):
+    """The mixed batch: the whole batch against T_roof = max(F / F_peak, B / B_peak),
+    its prefill-only and decode-only parts each against their own roofline
+    (same pool, same descriptors, timed as separate calls), and the KV write of
+    its fresh rows."""
+    import torch
+    import kv_cache_attention_msa_amd as msa
+    import workloads as W
+    kv = wl.dense_pool("cuda")
+    f, b = work_of(wl)
+    ms, t, plan = run_workload(wl, steps, warmup, msa.KERNEL_PREFILL, pool_kv=kv)
+    dev_ms = sum(t[k][0] for k in (msa.KERNEL_PREFILL, msa.KERNEL_DECODE, msa.KERNEL_MERGE, msa.KERNEL_UPLOAD)) / steps
+    t_roof = max(f / (PEAK_BF16_TFLOPS * 1e12), b / (PEAK_HBM_GBS * 1e9)) * 1e3
+    per_kernel = {name: (t[k][0] / t[k][1] if t[k][1] else 0.0)
+                  for name, k in (("chunk_ms", msa.KERNEL_PREFILL), ("decode_ms", msa.KERNEL_DECODE),
+                                  ("merge_ms", msa.KERNEL_MERGE), ("upload_ms", msa.KERNEL_UPLOAD))}
+    pre_seqs, dec_seqs = W.mixed_parts(wl)
+    wp = W.subset(wl, pre_seqs, wl.name + "_prefill_part")
+    wd = W.subset(wl, dec_seqs, wl.name + "_decode_part")
+    fp, bp = work_of(wp)
+    msp, tp, _ = run_workload(wp, steps, warmup, msa.KERNEL_PREFILL, pool_kv=kv)
+    fd, bd = work_of(wd)
+    msd, td, _ = run_workload(wd, steps, warmup, msa.KERNEL_DECODE, pool_kv=kv)
+    mixed = {"workload": wl.name, "metric": "T_roof / T", "ms_per_step": ms, "device_ms_per_step": dev_ms,
+             "algorithmic_flops": f, "algorithmic_bytes": b, "T_roof_ms": t_roof,
+             "value": t_roof / ms, "roof_frac_device": t_roof / dev_ms, "kernels": per_kernel, "host_call_ms": plan,
+             "prefill_part": {"workload": wp.name, "sequences": len(pre_seqs), "total_q": wp.total_q,
+                              "ms_per_step": msp, "algorithmic_flops": fp, "algorithmic_bytes": bp,
+                              "roofline": mfma_roofline(wp, fp, tp, steps)},
+             "decode_part": {"workload": wd.name, "sequences": len(dec_seqs), "ms_per_step": msd,
+                             "algorithmic_flops": fd, "algorithmic_bytes": bd,
+                             "roofline": hbm_roofline(wd, bd, td)}}
+    fresh = W.fresh_kv(wl, seed=5)
+    b5 = write_bytes(wl, fresh)
+    ms5, k5w, k5, n5 = run_write(wl, fresh, steps, warmup, pool_kv=kv)
+    ach5 = b5 / (k5 * 1e-3) / 1e9 if n5 else None
+    write = {
+        "workload": wl.name + "_fresh", "metric": "KV write HBM GB/s", "value": b5 / (ms5 * 1e-3) / 1e9,
+        "unit": "GB/s", "ms_per_step": ms5, "algorithmic_bytes": b5, "segments": int(len(fresh.segs)),
+        "rows": fresh.rows,
+        "roofline": {"bound": "hbm", "achieved": ach5, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach5 / PEAK_HBM_GBS if ach5 else None,
+                     "traffic": traffic_for("write", wl.name + "_fresh"), "kernel": "msa_write",
+                     "kernel_ms": k5, "cache": "cold (1 GiB read between calls evicts the Infinity Cache)",
+                     "kernel_warm_ms": k5w, "achieved_warm": b5 / (k5w * 1e-3) / 1e9 if n5 else None,
+                     "kernel_ms_dist_cold": run_write.dists["cold"],
+                     "kernel_ms_dist_warm": run_write.dists["warm"], "_ref": "copy"},
+    }
+    del kv
+    torch.cuda.empty_cache()
+    return mixed, write
+
+
+def tiny_entry(wl, steps, warmup):
+    """The tiny fp32 case: launch-latency bound, so time only (no roofline fraction)."""
+    import kv_cache_attention_msa_amd as msa
+    f, b = work_of(wl)
+    ms, t, plan = run_workload(wl, steps, warmup, msa.KERNEL_FP32)
+    k_ms, k_n = t[msa.KERNEL_FP32]
+    return {"workload": wl.name, "dtype": "f32", "ms_per_step": ms, "kernel_ms": k_ms / max(k_n, 1),
+            "kernel_ms_dist": t["dist"], "algorithmic_flops": f, "algorithmic_bytes": b, "host_call_ms": plan}
 
 
 if __name__ == "__main__":

@@ -121,14 +121,20 @@ typedef struct {
  *
  *  q            device [total_q][num_q_heads][head_dim], pool dtype
  *  block_table  device int32 [block_table_len]; entries are pool block ids in
- *               [0, num_blocks), read on `stream` (an id out of range is
- *               clamped into the pool on the device, not reported)
+ *               [0, num_blocks), read on `stream`.  An id out of range is
+ *               clamped into the pool on the device and not reported, unless
+ *               MSA_OPT_CHECK_BLOCK_IDS is set (then the call fails with
+ *               MSA_ERR_INVALID_ARG before any attention kernel)
  *  out          device [total_q][num_q_heads][head_dim], pool dtype
  *  lse          device float32 [total_q][num_q_heads], or NULL
  *  stream       hipStream_t to enqueue on (NULL = default stream)
  *
  * Work is enqueued asynchronously on `stream`; results are valid once it
- * completes.  A pool serialises its workspace on one stream at a time: calls
+ * completes.  Values: the q, K and V elements a call reads must be finite;
+ * a NaN or infinity among them gives unspecified out and lse for the rows
+ * that see it (the bf16 kernels are built without NaN-propagation guarantees
+ * in their max and exponent arithmetic).  Pool slots outside the segments are
+ * never read into the arithmetic, whatever they hold.  A pool serialises its workspace on one stream at a time: calls
  * on one pool must be issued from one host thread and, if they use different
  * streams, the caller must order those streams.  q, out and lse must not alias.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM, WORKSPACE, HIP. */
@@ -179,7 +185,9 @@ int msa_forward_noalloc(const void* q, const msa_seg_desc* desc, const int32_t* 
  *  src_rows      host int32 [num_segs]: row of k_src/v_src holding token 0 of
  *                segment s; 0 <= src_rows[s], src_rows[s] + len <= num_src_rows
  *  block_table   device int32 [block_table_len], as for msa_forward; entries are
- *                clamped into [0, num_blocks) on the device
+ *                clamped into [0, num_blocks) on the device, or checked with
+ *                MSA_OPT_CHECK_BLOCK_IDS (then an out-of-range id fails the
+ *                call with MSA_ERR_INVALID_ARG before the write kernel)
  *  stream        hipStream_t to enqueue on; ordered with msa_forward calls on
  *                the same pool and stream
  *
@@ -201,6 +209,15 @@ const char* msa_last_error(void);
                                    KV work and the merge); 0: automatic            */
 #define MSA_OPT_NUM_CUS      3  /* >0: compute-unit count the planner balances for;
                                    0: the device's                                  */
+#define MSA_OPT_CHECK_BLOCK_IDS 4 /* 1: before any attention or write kernel, check on
+                                   the device that every block-table entry the call
+                                   reads names a pool block in [0, num_blocks); if
+                                   one does not, the call returns MSA_ERR_INVALID_ARG
+                                   (naming the first such block-table index) with
+                                   only the plan copy into the library's own buffer
+                                   enqueued.  Synchronises the stream on every call.
+                                   0 (default): ids are clamped into the pool on
+                                   the device, without a report                     */
 
 int msa_pool_set_option(msa_pool* pool, int32_t option, int64_t value);
 

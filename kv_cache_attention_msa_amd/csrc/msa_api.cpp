@@ -87,6 +87,7 @@ struct msa_pool {
 
   // options
   bool timing = false;
+  bool check_ids = false;
   int32_t split_blocks = 0;
   int32_t num_cus_override = 0;
 
@@ -102,6 +103,7 @@ struct msa_pool {
   hipEvent_t stage_done[kSlots] = {};
   bool stage_pending[kSlots] = {};
   int next_slot = 0;
+  int last_slot = 0;                   // slot of the most recent upload
   void* d_plan = nullptr;
   size_t plan_cap = 0;
   // partial results of KV-split tiles
@@ -238,6 +240,7 @@ int stage_and_upload(msa_pool* p, hipStream_t stream, size_t bytes, int32_t n_bl
   if (rc) return rc;
   const int slot = p->next_slot;
   p->next_slot = (p->next_slot + 1) % msa_pool::kSlots;
+  p->last_slot = slot;
   rc = ensure_stage(p, slot, bytes);
   if (rc) return rc;
   fill((char*)p->h_stage[slot]);
@@ -309,13 +312,41 @@ int refresh_cus(msa_pool* p, const msa_seg_desc* desc) {
 // Where each part of a call's plan sits in the packed plan buffer, and the
 // size of its partial-result area.
 struct PlanLayout {
-  size_t off_blocks, off_qpos, off_items[3], off_merge, plan_bytes;
+  size_t off_blocks, off_qpos, off_items[3], off_merge, off_check, plan_bytes;
   size_t off_part_lse, part_bytes;
 };
 
 // The block list is followed by kBlockPad zero entries so that a kernel may
 // always read the entries of a step (their valid counts are ignored).
 constexpr size_t kBlockPad = 4;
+
+// Two result words of the optional block-id check (count, smallest bad
+// block-table index) close every packed plan; the host writes their start
+// values and the upload copies them into device memory.
+constexpr size_t kCheckBytes = 256;
+
+void pack_check_words(char* h) {
+  const int32_t init[2] = {0, INT32_MAX};
+  memset(h, 0, kCheckBytes);
+  memcpy(h, init, sizeof(init));
+}
+
+// With MSA_OPT_CHECK_BLOCK_IDS: after the upload, count the block-list entries
+// whose block-table entry is out of range (reading the host-packed list at
+// `src`), read the result back and fail the call if there is any.  The call
+// then has enqueued only the upload (into the library's own buffer).
+int check_block_ids(msa_pool* p, hipStream_t stream, const void* src, int32_t n_blocks, const int32_t* block_table,
+                    int32_t* d_result) {
+  int e = launch_check_ids(src, n_blocks, block_table, p->desc.num_blocks, d_result, stream);
+  if (e != hipSuccess) return hip_error((hipError_t)e, "kernel launch");
+  int32_t r[2] = {0, 0};
+  MSA_HIP(hipMemcpyAsync(r, d_result, sizeof(r), hipMemcpyDeviceToHost, stream));
+  MSA_HIP(hipStreamSynchronize(stream));
+  if (r[0] != 0)
+    return set_error(MSA_ERR_INVALID_ARG, "%d block-list entries name pool block ids outside [0, %d); the first is "
+                     "block_table[%d]", r[0], p->desc.num_blocks, r[1]);
+  return MSA_OK;
+}
 
 PlanLayout plan_layout(const Plan& plan, int D) {
   PlanLayout L{};
@@ -330,6 +361,8 @@ PlanLayout plan_layout(const Plan& plan, int D) {
   }
   L.off_merge = off;
   off = align_up(off + plan.merges.size() * sizeof(MergeItem), 256);
+  L.off_check = off;
+  off += kCheckBytes;
   L.plan_bytes = off;
   L.off_part_lse = align_up((size_t)plan.part_rows * D * sizeof(float), 256);
   L.part_bytes = plan.part_rows > 0 ? L.off_part_lse + align_up((size_t)plan.part_rows * sizeof(float), 256) : 0;
@@ -344,6 +377,7 @@ void pack_plan(const Plan& plan, const PlanLayout& L, char* h) {
     if (!plan.items[k].empty())
       memcpy(h + L.off_items[k], plan.items[k].data(), plan.items[k].size() * sizeof(WorkItem));
   if (!plan.merges.empty()) memcpy(h + L.off_merge, plan.merges.data(), plan.merges.size() * sizeof(MergeItem));
+  pack_check_words(h + L.off_check);
 }
 
 // Enqueue the attention kernels of a planned call whose plan is in device
@@ -483,6 +517,7 @@ int msa_pool_set_option(msa_pool* p, int32_t option, int64_t value) {
   if (!p) return set_error(MSA_ERR_INVALID_ARG, "pool is NULL");
   switch (option) {
     case MSA_OPT_TIMING: p->timing = value != 0; return MSA_OK;
+    case MSA_OPT_CHECK_BLOCK_IDS: p->check_ids = value != 0; return MSA_OK;
     case MSA_OPT_SPLIT_BLOCKS:
       if (value < 0 || value > (1 << 30)) return set_error(MSA_ERR_INVALID_ARG, "bad split_blocks");
       p->split_blocks = (int32_t)value;
@@ -585,6 +620,11 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
   rc = stage_and_upload(p, stream, L.plan_bytes, (int32_t)plan.blocks.size(), block_table,
                         [&](char* h) { pack_plan(plan, L, h); });
   if (rc) return rc;
+  if (p->check_ids) {
+    rc = check_block_ids(p, stream, p->h_stage_dev[p->last_slot], (int32_t)plan.blocks.size(), block_table,
+                         (int32_t*)((char*)p->d_plan + L.off_check));
+    if (rc) return rc;
+  }
   return launch_attention(p, desc, L, (char*)p->d_plan, (char*)p->d_part, q, out, lse, stream, p->timing);
 }
 
@@ -628,6 +668,10 @@ int msa_forward_noalloc(const void* q, const msa_seg_desc* desc, const int32_t* 
   int e = launch_upload(stage, dplan, L.plan_bytes, (int32_t)plan.blocks.size(), block_table, p->desc.num_blocks,
                         stream);
   if (e != hipSuccess) return hip_error((hipError_t)e, "kernel launch");
+  if (p->check_ids) {
+    rc = check_block_ids(p, stream, stage, (int32_t)plan.blocks.size(), block_table, (int32_t*)(dplan + L.off_check));
+    if (rc) return rc;
+  }
   return launch_attention(p, desc, L, dplan, dpart, q, out, lse, stream, false);
 }
 
@@ -691,12 +735,19 @@ int msa_write_kv(msa_pool* p, const void* k_src, const void* v_src, int32_t num_
   hipStream_t stream = (hipStream_t)stream_;
   DeviceGuard guard(p->desc.device);
   if (!guard.ok) return set_error(MSA_ERR_HIP, "cannot select device %d", p->desc.device);
-  const size_t bytes = align_up(ent.size() * sizeof(BlockEntry), 256);
+  const size_t off_check = align_up(ent.size() * sizeof(BlockEntry), 256);
+  const size_t bytes = off_check + kCheckBytes;
   int rc = stage_and_upload(p, stream, bytes, (int32_t)ent.size(), block_table, [&](char* h) {
     memcpy(h, ent.data(), ent.size() * sizeof(BlockEntry));
-    memset(h + ent.size() * sizeof(BlockEntry), 0, bytes - ent.size() * sizeof(BlockEntry));
+    memset(h + ent.size() * sizeof(BlockEntry), 0, off_check - ent.size() * sizeof(BlockEntry));
+    pack_check_words(h + off_check);
   });
   if (rc) return rc;
+  if (p->check_ids) {
+    rc = check_block_ids(p, stream, p->h_stage_dev[p->last_slot], (int32_t)ent.size(), block_table,
+                         (int32_t*)((char*)p->d_plan + off_check));
+    if (rc) return rc;
+  }
   WriteArgs a{};
   a.k_src = k_src;
   a.v_src = v_src;

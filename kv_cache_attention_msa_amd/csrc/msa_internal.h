@@ -138,5 +138,11 @@ int launch_write(const WriteArgs& a, int row_bytes, void* stream);
 // through `block_table`; ids outside [0, num_blocks) are clamped into range.
 int launch_upload(const void* src, void* dst, size_t bytes, int32_t n_blocks, const int32_t* block_table,
                   int32_t num_blocks, void* stream);
+// With MSA_OPT_CHECK_BLOCK_IDS: counts the first n_blocks entries of the
+// host-packed block list at `src` whose block-table entry is out of range
+// into result[0] and keeps the smallest such block-table index in result[1]
+// (device words that start at 0 and INT32_MAX).
+int launch_check_ids(const void* src, int32_t n_blocks, const int32_t* block_table, int32_t num_blocks,
+                     int32_t* result, void* stream);
 
 }  // namespace msa

@@ -30,6 +30,33 @@ __global__ __launch_bounds__(256) void msa_upload_kernel(const uint4* __restrict
   }
 }
 
+// Optional block-id check: counts the entries of a host-packed block list
+// whose block-table entry holds an id outside [0, num_blocks), and keeps the
+// smallest such block-table index.  result[0] must start at 0 and result[1]
+// at INT32_MAX.
+__global__ __launch_bounds__(256) void msa_check_ids_kernel(const BlockEntry* __restrict__ src, int32_t n_blocks,
+                                                             const int32_t* __restrict__ block_table,
+                                                             int32_t num_blocks, int32_t* result) {
+  const uint32_t mask = (1u << kBtIndexBits) - 1u;
+  for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n_blocks; i += gridDim.x * blockDim.x) {
+    const int32_t idx = (int32_t)((uint32_t)src[i].bt_valid & mask);
+    const int32_t id = block_table[idx];
+    if (id < 0 || id >= num_blocks) {
+      atomicAdd(&result[0], 1);
+      atomicMin(&result[1], idx);
+    }
+  }
+}
+
+int launch_check_ids(const void* src, int32_t n_blocks, const int32_t* block_table, int32_t num_blocks,
+                     int32_t* result, void* stream) {
+  if (n_blocks <= 0) return 0;
+  const int blocks = std::min((n_blocks + 255) / 256, 1024);
+  hipLaunchKernelGGL(msa_check_ids_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const BlockEntry*)src,
+                     n_blocks, block_table, num_blocks, result);
+  return (int)hipGetLastError();
+}
+
 int launch_upload(const void* src, void* dst, size_t bytes, int32_t n_blocks, const int32_t* block_table,
                   int32_t num_blocks, void* stream) {
   const size_t n = bytes / 16;

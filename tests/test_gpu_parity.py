@@ -247,3 +247,37 @@ def test_benchmark_config_full_size(cfg):
     print(f"[parity] config {cfg} ({wl.name}): rows {m['rows']}, out max-abs {m['out_max_abs']:.3e} "
           f"mean-abs {m['out_mean_abs']:.3e}, lse max-abs {m['lse_max_abs']:.3e} mean-abs {m['lse_mean_abs']:.3e}",
           flush=True)
+
+
+def test_block_id_check_option():
+    """MSA_OPT_CHECK_BLOCK_IDS: a table of valid ids gives the usual result; an
+    entry outside [0, num_blocks) fails the call with MSA_ERR_INVALID_ARG
+    naming the first bad block-table index, for msa_forward and
+    msa_forward_noalloc, before any attention kernel writes out.  Without the
+    option the same table is clamped on the device and the call succeeds."""
+    wl = W.random_case(64, batch=3, H_q=8, H_kv=2, d=128, max_ctx=500)
+    case = GpuCase(wl)
+    try:
+        case.pool.set_option(msa.OPT_CHECK_BLOCK_IDS, 1)
+        out, lse = case.run()
+        ref_out, ref_lse = oracle_result(wl)
+        compare(wl, out, lse, ref_out, ref_lse)
+        used = sorted({int(s[2]) for s in wl.segs if s[1] > 0})
+        bad_idx = used[len(used) // 2]
+        for bad in (wl.num_blocks, -1, 1 << 27):
+            bt = case.bt.clone()
+            bt[bad_idx] = bad
+            bt[used[-1]] = wl.num_blocks + 7
+            for fn in (msa.forward, msa.forward_noalloc):
+                case.out.fill_(float("nan"))
+                with pytest.raises(msa.MsaError) as ei:
+                    fn(case.q, case.desc, bt, case.pool, case.out, case.lse)
+                torch.cuda.synchronize()
+                assert ei.value.code == msa.ERR_INVALID_ARG
+                assert f"block_table[{min(bad_idx, used[-1])}]" in str(ei.value), str(ei.value)
+                assert torch.isnan(case.out.float()).all(), "an attention kernel ran after the failed check"
+        case.pool.set_option(msa.OPT_CHECK_BLOCK_IDS, 0)
+        msa.forward(case.q, case.desc, bt, case.pool, case.out, case.lse)
+        torch.cuda.synchronize()
+    finally:
+        case.close()

@@ -184,3 +184,26 @@ def test_mixed_full_size_write_then_attend(mixed):
     rows = np.unique(np.concatenate([rng.choice(wl.total_q, 48, replace=False),
                                      wl.q_offsets[1:] - 1]))
     _write_then_attend(wl, fresh, rows=rows)
+
+
+def test_write_block_id_check_option():
+    """MSA_OPT_CHECK_BLOCK_IDS on msa_write_kv: an out-of-range destination id
+    fails the call before the write kernel, and the pool is left unchanged."""
+    wl = W.random_case(505, batch=2, H_q=8, H_kv=2, d=128, max_ctx=300, max_chunk=60)
+    fresh = W.fresh_kv(wl, seed=505)
+    K, V = wl.dense_pool("cuda")
+    K0, V0 = _np_bits(K), _np_bits(V)
+    pool = _pool_for(wl, K, V)
+    try:
+        pool.set_option(msa.OPT_CHECK_BLOCK_IDS, 1)
+        bt = _bt(wl)
+        dst = int(fresh.segs[0, 2])
+        bt[dst] = wl.num_blocks + 3
+        with pytest.raises(msa.MsaError) as ei:
+            msa.write_kv(pool, fresh.k.cuda(), fresh.v.cuda(), fresh.segs, fresh.src_rows, bt)
+        torch.cuda.synchronize()
+        assert ei.value.code == msa.ERR_INVALID_ARG and "block_table[" in str(ei.value)
+        np.testing.assert_array_equal(_np_bits(K), K0)
+        np.testing.assert_array_equal(_np_bits(V), V0)
+    finally:
+        pool.close()

@@ -30,7 +30,7 @@ workload definitions leave open are N(0,1)*0.5 rounded to bf16.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -323,6 +323,33 @@ def config5(seed=5):
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def subset(wl, seqs, name):
+    """The sequences ``seqs`` of ``wl`` (in that order) as a workload of their
+    own, over the same pool and block table (e.g. the prefill-only or the
+    decode-only part of the mixed batch)."""
+    rows, q_pos, segs = [], [], []
+    q_off, s_off = [0], [0]
+    for b in seqs:
+        r0, r1 = int(wl.q_offsets[b]), int(wl.q_offsets[b + 1])
+        rows.append(np.arange(r0, r1, dtype=np.int64))
+        q_pos.extend(wl.q_pos[r0:r1].tolist())
+        segs.extend(wl.segs[wl.seg_offsets[b]:wl.seg_offsets[b + 1]].tolist())
+        q_off.append(q_off[-1] + r1 - r0)
+        s_off.append(len(segs))
+    idx = torch.from_numpy(np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64))
+    return replace(wl, name=name, q=wl.q[idx].contiguous(),
+                   q_offsets=np.array(q_off, dtype=np.int32), q_pos=np.array(q_pos, dtype=np.int32).reshape(-1),
+                   seg_offsets=np.array(s_off, dtype=np.int32),
+                   segs=np.array(segs, dtype=np.int32).reshape(-1, 4), meta=dict(wl.meta, subset_of=wl.name))
+
+
+def mixed_parts(wl):
+    """Sequence indices of the prefill chunks and of the decode tokens of the
+    mixed batch (configuration 5), in batch order."""
+    kinds = wl.meta["kinds"]
+    return ([b for b, k in enumerate(kinds) if k == "prefill"], [b for b, k in enumerate(kinds) if k == "decode"])
 
 
 # --------------------------------------------------------------------------
