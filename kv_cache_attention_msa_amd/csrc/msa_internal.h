@@ -13,7 +13,7 @@ namespace msa {
 constexpr int kBlock = MSA_BLOCK_SIZE;
 constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per prefill tile
 constexpr int kDecodeMRows = 8;      // pairs per decode tile (at most 8 of the 16 MFMA columns)
-constexpr int kFp32MRows = 64;       // pairs per fp32 tile
+constexpr int kFp32MRows = 16;       // pairs per fp32 tile (one wave each)
 constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accepted
 constexpr int kBtIndexBits = 28;     // index bits in BlockEntry::bt_valid
 constexpr int kMaxPoolBlocks = 1 << kBtIndexBits;

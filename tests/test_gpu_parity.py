@@ -54,6 +54,8 @@ def test_random_fp32_cases():
     for seed in range(3):
         _check(W.random_case(40 + seed, batch=3, H_q=4, H_kv=2, d=64, dtype="fp32"))
         _check(W.random_case(50 + seed, batch=2, H_q=2, H_kv=1, d=128, dtype="fp32"), split_blocks=2)
+    # a GQA group (32) larger than the fp32 tile's 16 waves: each wave takes several rows
+    _check(W.random_case(55, batch=2, H_q=32, H_kv=1, d=64, dtype="fp32"))
 
 
 def test_asymcache_layout():
