@@ -73,9 +73,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+// K operands of rows `row` and `row + 32` at chunk c: both rows have the same
+// swizzle (it depends on row % 16), so one address serves both.
 template <int D>
-__device__ __forceinline__ bf16x8 ld_k(const StepTile<D>& tl, int row, int c) {
-  return as_bf16x8(tl.k[row][c ^ k_swz<D>(row)]);
+__device__ __forceinline__ void ld_k2(const StepTile<D>& tl, int row, int c, bf16x8& k0, bf16x8& k1) {
+  const uint4* p = &tl.k[row][c ^ k_swz<D>(row)];
+  k0 = as_bf16x8(p[0]);
+  k1 = as_bf16x8(p[32 * (D / 8)]);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -179,15 +183,22 @@ __device__ __forceinline__ void dma_step(const KernelArgs& a, int kv_head, const
 
 // Scores of one 32-row half for a step: s{kb} register r holds key
 // 32kb + 8(r/4) + 4h + r%4 (block 2kb + r/8, slot 8((r/4)&1) + 4h + r%4).
+// Within a block, positions run with the slot, so a key of block b is
+// visible to the row iff its slot is below lim(b) = min(valid(b),
+// qpos - pos0(b) + 1) (valid(b) when not causal): one compare per score.
+__device__ __forceinline__ int block_lim(const StepMeta& m, int b, int qpos, bool causal) {
+  const int v = m.valid(b);
+  return causal ? min(v, qpos - m.pos0(b) + 1) : v;
+}
+
 __device__ __forceinline__ void mask_half(f32x16& s0, f32x16& s1, const StepMeta& m, int h, int qpos, bool causal) {
+  const int l0 = block_lim(m, 0, qpos, causal), l1 = block_lim(m, 1, qpos, causal);
+  const int l2 = block_lim(m, 2, qpos, causal), l3 = block_lim(m, 3, qpos, causal);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int slot = 8 * ((r >> 2) & 1) + 4 * h + (r & 3);
-    const int b0 = r >> 3, b1 = 2 + (r >> 3);
-    const bool ok0 = slot < m.valid(b0) && (!causal || m.pos0(b0) + slot <= qpos);
-    const bool ok1 = slot < m.valid(b1) && (!causal || m.pos0(b1) + slot <= qpos);
-    s0[r] = ok0 ? s0[r] : kNegInf;
-    s1[r] = ok1 ? s1[r] : kNegInf;
+    s0[r] = slot < ((r >> 3) ? l1 : l0) ? s0[r] : kNegInf;
+    s1[r] = slot < ((r >> 3) ? l3 : l2) ? s1[r] : kNegInf;
   }
 }
 
@@ -313,8 +324,8 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
   f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 k0 = ld_k<D>(tl, col, 2 * ks + h);
-    const bf16x8 k1 = ld_k<D>(tl, 32 + col, 2 * ks + h);
+    bf16x8 k0, k1;
+    ld_k2<D>(tl, col, 2 * ks + h, k0, k1);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qop[ks], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qop[ks], s1, 0, 0, 0);
   }
