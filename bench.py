@@ -459,6 +459,94 @@ def latency_report(src, dst, command):
     print(f"wrote {dst}")
 
 
+def evict_sweep(report=None, sizes=(4000, 5000, 6000, 7000, 8000, 9000, 10000), cycles=2000, seed=0):
+    """Eviction time against the number of cached blocks (the comparison of the
+    paper's Figure 9): per eviction, the lowest-score block leaves and a new
+    one is cached, with two hits on random blocks in between.  Timed: the
+    library's O(log n) index (pop + insert), the same index evicting by its
+    O(n) rescoring scan (scan_min + remove + insert), the O(n) oracle in
+    Python, and an O(1) LRU list (Python OrderedDict) for scale.  Host only."""
+    import collections
+    import numpy as np
+    import kv_cache_attention_msa_amd as msa
+    from oracle import EvictOracle
+    k = [12.0, 0.4, 0.2, 0.05, 0.06]
+    s_decay, lam = 50.0, 4.0
+    model = msa.LatencyModel.from_coefficients(k)
+    rows = []
+    for n in sizes:
+        rng = np.random.default_rng(seed + n)
+        pos = rng.integers(0, 512, size=(n + cycles, 2)).astype(float)
+        hits = rng.integers(0, n, size=(cycles, 2))
+        res = {"blocks": n}
+        for kind in ("heap", "scan", "oracle", "lru"):
+            cyc = cycles if kind != "oracle" else max(20, cycles // 50)
+            idx = msa.EvictIndex(model, s_decay, lam) if kind in ("heap", "scan") else None
+            o = EvictOracle(k, s_decay, lam) if kind == "oracle" else None
+            lru = collections.OrderedDict() if kind == "lru" else None
+            live = []
+            for b in range(n):
+                t = b * 0.01
+                if idx is not None:
+                    idx.insert(b, pos[b, 0], pos[b, 1], t)
+                elif o is not None:
+                    o.insert(b, pos[b, 0], pos[b, 1], t)
+                else:
+                    lru[b] = t
+                live.append(b)
+            now, spent = n * 0.01, 0.0
+            warm = cyc // 10    # untimed first evictions (caches, allocator)
+            for c in range(cyc):
+                now += 0.01
+                for h in hits[c]:
+                    b = live[int(h) % len(live)]
+                    if idx is not None:
+                        idx.touch(b, now)
+                    elif o is not None:
+                        o.touch(b, now)
+                    else:
+                        lru.move_to_end(b)
+                nb = n + c
+                t0 = time.perf_counter()
+                if kind == "heap":
+                    gone, _ = idx.pop(now)
+                    idx.insert(nb, pos[nb, 0], pos[nb, 1], now)
+                elif kind == "scan":
+                    gone, _ = idx.scan_min(now)
+                    idx.remove(gone)
+                    idx.insert(nb, pos[nb, 0], pos[nb, 1], now)
+                elif kind == "oracle":
+                    gone, _ = o.pop(now)
+                    o.insert(nb, pos[nb, 0], pos[nb, 1], now)
+                else:
+                    gone, _ = lru.popitem(last=False)
+                    lru[nb] = now
+                if c >= warm:
+                    spent += time.perf_counter() - t0
+                live[live.index(gone)] = nb
+            res[kind + "_us"] = spent / (cyc - warm) * 1e6
+            if idx is not None:
+                idx.close()
+        rows.append(res)
+        print(json.dumps(res), flush=True)
+    if report:
+        lines = ["# Eviction time against cached blocks (host CPU)", "",
+                 "Command (run from the repository root):", "", "    python bench.py --evict-sweep --report " + report, "",
+                 f"Per eviction: the lowest-score block leaves and a new one is cached (two hits on random blocks in "
+                 f"between, not timed); score c * n * min(1, lambda exp(-x / s)) with lambda {lam}, s {s_decay}; mean of "
+                 f"{cycles} evictions ({max(20, cycles // 50)} for the Python oracle), the first tenth untimed. "
+                 f"The library's figures include two (index) or three (scan) Python-to-C calls per eviction, about "
+                 f"1 us each, so the O(log n) work itself is a fraction of its column. CPU: {cpu_model()}.", "",
+                 "| cached blocks | O(log n) index (us) | O(n) rescoring scan, native (us) | O(n) oracle, Python (us) | O(1) LRU, Python (us) |",
+                 "|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['blocks']} | {r['heap_us']:.2f} | {r['scan_us']:.1f} | {r['oracle_us']:.0f} | {r['lru_us']:.2f} |")
+        with open(report, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {report}")
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,10 +574,15 @@ def main():
     ap.add_argument("--latency-out", help="with --latency-model: also write the full result (JSON) here")
     ap.add_argument("--latency-batch", type=int, default=16, help="requests per step for --latency-model")
     ap.add_argument("--latency-report", help="summarise a --latency-out JSON into --report (no GPU needed)")
+    ap.add_argument("--evict-sweep", action="store_true",
+                    help="eviction time against 4-10 x 10^3 cached blocks (host only; with --report, a summary)")
     args = ap.parse_args()
     if args.latency_report:
         latency_report(args.latency_report, args.report,
                        args.command[0] if args.command else f"python bench.py --latency-model --latency-out {args.latency_report}")
+        return
+    if args.evict_sweep:
+        evict_sweep(args.report)
         return
     if args.report:
         write_report(args)

@@ -16,7 +16,7 @@ import numpy as np
 
 __all__ = [
     "MsaError", "Pool", "SegDesc", "forward", "forward_noalloc", "write_kv", "plan_debug", "library_path", "load_library",
-    "LatencyModel", "latency_fit", "chunk_blocks",
+    "LatencyModel", "latency_fit", "chunk_blocks", "EvictIndex", "lambda_from_lifespan",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
     "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS", "OPT_CHECK_BLOCK_IDS",
@@ -34,6 +34,9 @@ EXPORTED_SYMBOLS = (
     "msa_write_kv", "msa_last_error",
     "msa_pool_set_option", "msa_pool_kernel_time", "msa_pool_kernel_samples", "msa_plan_debug",
     "msa_latency_fit", "msa_latency_eval", "msa_latency_delta_b", "msa_chunk_blocks",
+    "msa_evict_create", "msa_evict_destroy", "msa_evict_insert", "msa_evict_touch", "msa_evict_set_position",
+    "msa_evict_remove", "msa_evict_pop", "msa_evict_scan_min", "msa_evict_score", "msa_evict_set_lambda",
+    "msa_evict_lambda_from_lifespan", "msa_evict_size",
 )
 
 _ERR_NAMES = {ERR_INVALID_ARG: "INVALID_ARG", ERR_UNSUPPORTED: "UNSUPPORTED", ERR_OOM: "OOM",
@@ -105,6 +108,18 @@ def load_library():
     lib.msa_latency_eval.argtypes = [ctypes.POINTER(_LatencyModel), D, D, D, D, ctypes.POINTER(D)]
     lib.msa_latency_delta_b.argtypes = [ctypes.POINTER(_LatencyModel), D, D, ctypes.POINTER(D)]
     lib.msa_chunk_blocks.argtypes = [ctypes.POINTER(_LatencyModel), D, D, D, I32, D, ctypes.POINTER(I32)]
+    lib.msa_evict_create.argtypes = [ctypes.POINTER(_LatencyModel), D, D, ctypes.POINTER(P)]
+    lib.msa_evict_destroy.argtypes = [P]
+    lib.msa_evict_insert.argtypes = [P, I64, D, D, D]
+    lib.msa_evict_touch.argtypes = [P, I64, D]
+    lib.msa_evict_set_position.argtypes = [P, I64, D, D]
+    lib.msa_evict_remove.argtypes = [P, I64]
+    lib.msa_evict_pop.argtypes = [P, D, ctypes.POINTER(I64), ctypes.POINTER(D)]
+    lib.msa_evict_scan_min.argtypes = [P, D, ctypes.POINTER(I64), ctypes.POINTER(D)]
+    lib.msa_evict_score.argtypes = [P, I64, D, ctypes.POINTER(D)]
+    lib.msa_evict_set_lambda.argtypes = [P, D, D]
+    lib.msa_evict_lambda_from_lifespan.argtypes = [D, D, D, D, ctypes.POINTER(D)]
+    lib.msa_evict_size.argtypes = [P, ctypes.POINTER(I64)]
     for name in EXPORTED_SYMBOLS:
         if name != "msa_last_error":
             getattr(lib, name).restype = ctypes.c_int
@@ -303,6 +318,14 @@ class LatencyModel:
     def __init__(self, c: _LatencyModel):
         self.c = c
 
+    @classmethod
+    def from_coefficients(cls, k):
+        """A model with given k1..k5 (no fit)."""
+        c = _LatencyModel()
+        for i, v in enumerate(k):
+            c.k[i] = float(v)
+        return cls(c)
+
     @property
     def k(self):
         return list(self.c.k)
@@ -336,6 +359,74 @@ def chunk_blocks(model: LatencyModel, l1, q1, l2, remaining: int, budget: float)
     _check(load_library().msa_chunk_blocks(ctypes.byref(model.c), l1, q1, l2, int(remaining), budget,
                                            ctypes.byref(c)))
     return c.value
+
+
+class EvictIndex:
+    """Eviction order of cached KV blocks (see include/msa_evict.h): the block of
+    lowest score c * n * min(1, lambda * exp(-x / s)) is evicted first, with c
+    the Eq. 5 recomputation cost from ``model``."""
+
+    def __init__(self, model: LatencyModel, s: float, lam: float):
+        h = ctypes.c_void_p()
+        _check(load_library().msa_evict_create(ctypes.byref(model.c), float(s), float(lam), ctypes.byref(h)))
+        self.handle = h
+
+    def insert(self, block: int, l1: float, q1: float, now: float):
+        _check(load_library().msa_evict_insert(self.handle, int(block), float(l1), float(q1), float(now)))
+
+    def touch(self, block: int, now: float):
+        _check(load_library().msa_evict_touch(self.handle, int(block), float(now)))
+
+    def set_position(self, block: int, l1: float, q1: float):
+        _check(load_library().msa_evict_set_position(self.handle, int(block), float(l1), float(q1)))
+
+    def remove(self, block: int):
+        _check(load_library().msa_evict_remove(self.handle, int(block)))
+
+    def _pick(self, fn, now):
+        b, sc = ctypes.c_int64(), ctypes.c_double()
+        _check(fn(self.handle, float(now), ctypes.byref(b), ctypes.byref(sc)))
+        return b.value, sc.value
+
+    def pop(self, now: float):
+        """Evict: (block, score) of the lowest score at ``now``."""
+        return self._pick(load_library().msa_evict_pop, now)
+
+    def scan_min(self, now: float):
+        """(block, score) that pop would take, by rescoring every block (O(n))."""
+        return self._pick(load_library().msa_evict_scan_min, now)
+
+    def score(self, block: int, now: float) -> float:
+        sc = ctypes.c_double()
+        _check(load_library().msa_evict_score(self.handle, int(block), float(now), ctypes.byref(sc)))
+        return sc.value
+
+    def set_lambda(self, lam: float, now: float):
+        _check(load_library().msa_evict_set_lambda(self.handle, float(lam), float(now)))
+
+    def __len__(self):
+        n = ctypes.c_int64()
+        _check(load_library().msa_evict_size(self.handle, ctypes.byref(n)))
+        return n.value
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            load_library().msa_evict_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lambda_from_lifespan(tau: float, tau0: float, alpha: float, beta: float) -> float:
+    """Eq. 10: lambda = exp((tau - tau0) / beta - tau / alpha)."""
+    lam = ctypes.c_double()
+    _check(load_library().msa_evict_lambda_from_lifespan(float(tau), float(tau0), float(alpha), float(beta),
+                                                          ctypes.byref(lam)))
+    return lam.value
 
 
 def plan_debug(seg_desc: SegDesc, num_kv_heads: int, head_dim: int, dtype: int = BF16,

@@ -23,7 +23,7 @@ PEAKS_LIB = os.path.join(PKG, "libmsa_peaks.so")   # measurement probes (benchma
 PEAKS_SOURCE = os.path.join(HERE, "peaks", "msa_peaks.hip")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["msa_plan.cpp", "msa_api.cpp", "msa_latency.cpp"]
+HOST_SOURCES = ["msa_plan.cpp", "msa_api.cpp", "msa_latency.cpp", "msa_evict.cpp"]
 HIP_SOURCES = sorted(f for f in os.listdir(HERE) if f.endswith(".hip"))
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{HERE}", "-Wall", "-Wno-unused-function"]

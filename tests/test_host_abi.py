@@ -18,7 +18,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def test_library_exports_every_declared_symbol():
     lib = msa.load_library()
-    text = open(HEADER).read() + open(os.path.join(os.path.dirname(HEADER), "msa_latency.h")).read()
+    text = "".join(open(os.path.join(os.path.dirname(HEADER), h)).read()
+                   for h in ("msa.h", "msa_latency.h", "msa_evict.h"))
     declared = set(re.findall(r"^(?:int|const char\*)\s+(msa_\w+)\s*\(", text, flags=re.M))
     assert declared == set(msa.EXPORTED_SYMBOLS)
     for name in declared:
