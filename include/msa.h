@@ -245,7 +245,7 @@ int msa_pool_kernel_samples(msa_pool* pool, int32_t kind, double* out, int32_t m
 
 /* One work item of a plan (as the kernels see it). */
 typedef struct {
-  int32_t kind;       /* MSA_KERNEL_PREFILL / DECODE / FP32                       */
+  int32_t kind;       /* MSA_KERNEL_PREFILL / DECODE / FP32: the work the item is  */
   int32_t seq;        /* sequence index                                          */
   int32_t kv_head;
   int32_t q_row0;     /* first query row                                         */
@@ -253,6 +253,9 @@ typedef struct {
   int32_t blk_begin;  /* [blk_begin, blk_end): entries of the block list          */
   int32_t blk_end;
   int32_t part_row;   /* -1: writes out/lse directly; else first partial row      */
+  int32_t launch;     /* kernel launch that runs it: as kind, except that a batch
+                         of prefill chunks and decode tokens runs its decode
+                         items in the MSA_KERNEL_PREFILL launch                 */
 } msa_plan_item;
 
 /* One entry of the position-ordered block list. */

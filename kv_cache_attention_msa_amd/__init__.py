@@ -70,7 +70,8 @@ class _LatencyModel(ctypes.Structure):
 
 
 PLAN_ITEM_DTYPE = np.dtype([("kind", "<i4"), ("seq", "<i4"), ("kv_head", "<i4"), ("q_row0", "<i4"),
-                            ("n_q", "<i4"), ("blk_begin", "<i4"), ("blk_end", "<i4"), ("part_row", "<i4")])
+                            ("n_q", "<i4"), ("blk_begin", "<i4"), ("blk_end", "<i4"), ("part_row", "<i4"),
+                            ("launch", "<i4")])
 PLAN_BLOCK_DTYPE = np.dtype([("bt_index", "<i4"), ("pos0", "<i4"), ("valid", "<i4")])
 
 _lib = None

@@ -586,7 +586,7 @@ int msa_plan_debug(const msa_seg_desc* desc, int32_t num_kv_heads, int32_t head_
   for (int k = 0; k < 3; ++k)
     for (const WorkItem& w : plan.items[k]) {
       if (n < max_items)
-        items[n] = msa_plan_item{k, w.seq, w.kv_head, w.q_row0, w.n_q, w.blk_begin, w.blk_end, w.part_row};
+        items[n] = msa_plan_item{w.kind, w.seq, w.kv_head, w.q_row0, w.n_q, w.blk_begin, w.blk_end, w.part_row, k};
       ++n;
     }
   *n_items = n;

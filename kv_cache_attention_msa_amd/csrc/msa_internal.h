@@ -45,6 +45,8 @@ struct WorkItem {
   int32_t part_row;  // -1: final output; else first row of this split's partials
   int32_t seq;
   int32_t q_min;     // smallest query position of the tile (causal fast path)
+  int32_t kind;      // kPrefill or kDecode: the work the item is (a decode item may
+                     // run in the chunk kernel's launch, see Plan::items)
 };
 
 // Rows of one tile that was split over KV: n_splits partials of n_mrows rows
@@ -66,7 +68,12 @@ enum Kind { kPrefill = MSA_KERNEL_PREFILL, kDecode = MSA_KERNEL_DECODE,
 struct Plan {
   std::vector<BlockEntry> blocks;
   std::vector<int32_t> q_pos;
-  std::vector<WorkItem> items[3];   // per kernel kind (prefill, decode, fp32)
+  // Per launch (prefill/chunk, decode, fp32 kernel).  When a batch holds both
+  // prefill chunks and decode tokens (bf16), the decode items go into the
+  // chunk kernel's launch, which runs them with the decode kernel's code: one
+  // attention launch for the batch, the decode items filling compute units
+  // beside the chunk items.
+  std::vector<WorkItem> items[3];
   std::vector<MergeItem> merges;
   int64_t part_rows = 0;            // partial rows (each head_dim floats + 1 lse)
   int32_t max_mrows[3] = {0, 0, 0}; // largest (query row, head) count of an item, per kind

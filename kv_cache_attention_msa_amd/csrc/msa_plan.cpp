@@ -36,6 +36,7 @@ namespace {
 
 struct Tile {
   int32_t kind, seq, q_min, q_row0, n_q, blk_begin, blk_end, nsplit;
+  int32_t launch;   // the launch (kernel) that runs the tile's items
 };
 
 // Largest block-count of one work item before the planner splits a tile.
@@ -226,14 +227,25 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
                                    [](int32_t v, const BlockEntry& e) { return v < e.pos0; });
         end = (int32_t)(it - plan.blocks.begin());
       }
-      tiles.push_back(Tile{kind, b, qmin, r, n, seq_blk0, end, 1});
+      tiles.push_back(Tile{kind, b, qmin, r, n, seq_blk0, end, 1, kind});
     }
   }
   plan.q_pos.assign(d->q_pos, d->q_pos + total_q);
 
+  // A batch of prefill chunks and decode tokens runs in one launch: the
+  // decode tiles join the chunk kernel's items (it runs them with the decode
+  // code), balanced together with them.
+  bool any_prefill = false, any_decode = false;
+  for (const Tile& t : tiles) {
+    any_prefill |= t.kind == kPrefill;
+    any_decode |= t.kind == kDecode;
+  }
+  if (any_prefill && any_decode)
+    for (Tile& t : tiles) t.launch = kPrefill;
+
   // Expand tiles over kv heads and split long ones.
   int64_t total_blocks[3] = {0, 0, 0};
-  for (const Tile& t : tiles) total_blocks[t.kind] += (int64_t)(t.blk_end - t.blk_begin) * cfg.num_kv_heads;
+  for (const Tile& t : tiles) total_blocks[t.launch] += (int64_t)(t.blk_end - t.blk_begin) * cfg.num_kv_heads;
   int64_t chunk[3];
   for (int k = 0; k < 3; ++k)
     chunk[k] = cfg.split_blocks > 0 ? cfg.split_blocks : auto_chunk(k, total_blocks[k], cfg.num_cus);
@@ -244,15 +256,15 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   int64_t part_rows = 0;
   for (Tile& t : tiles) {
     const int32_t nblk = t.blk_end - t.blk_begin;
-    const int64_t c = chunk[t.kind];
+    const int64_t c = chunk[t.launch];
     int32_t nsplit = 1;
     if (cfg.split_blocks > 0 ? nblk > c : nblk > c + c / 2) nsplit = (int32_t)((nblk + c - 1) / c);
     const int32_t align = (t.kind == kPrefill) ? 4 : 1;  // prefill consumes 4 blocks per step
     nsplit = std::max(1, std::min(nsplit, (nblk + align - 1) / align));
     t.nsplit = nsplit;
     const int32_t n_mrows = t.n_q * group;
-    plan.max_mrows[t.kind] = std::max(plan.max_mrows[t.kind], n_mrows);
-    n_items[t.kind] += (size_t)nsplit * cfg.num_kv_heads;
+    plan.max_mrows[t.launch] = std::max(plan.max_mrows[t.launch], n_mrows);
+    n_items[t.launch] += (size_t)nsplit * cfg.num_kv_heads;
     if (nsplit > 1) {
       n_merges += cfg.num_kv_heads;
       part_rows += (int64_t)nsplit * n_mrows * cfg.num_kv_heads;
@@ -267,10 +279,10 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   std::vector<int32_t>& bounds = plan_order();  // reused: split boundaries of one tile
   int32_t part = 0;
   for (const Tile& t : tiles) {
-    WorkItem*& wo = item_out[t.kind];
+    WorkItem*& wo = item_out[t.launch];
     if (t.nsplit == 1) {
       for (int32_t h = 0; h < cfg.num_kv_heads; ++h)
-        *wo++ = WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, t.q_min};
+        *wo++ = WorkItem{h, t.q_row0, t.n_q, t.blk_begin, t.blk_end, -1, t.seq, t.q_min, t.kind};
       continue;
     }
     // the same block ranges for every kv head
@@ -285,7 +297,7 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
     for (int32_t h = 0; h < cfg.num_kv_heads; ++h) {
       for (int32_t s = 0; s < t.nsplit; ++s)
         *wo++ = WorkItem{h, t.q_row0, t.n_q, t.blk_begin + bounds[s], t.blk_begin + bounds[s + 1],
-                         part + s * n_mrows, t.seq, t.q_min};
+                         part + s * n_mrows, t.seq, t.q_min, t.kind};
       *merge_out++ = MergeItem{h, t.q_row0, t.n_q, part, t.nsplit, n_mrows, 0, 0};
       part += t.nsplit * n_mrows;
     }

@@ -26,7 +26,14 @@
 // Each block's buffer resource covers only its valid slots: DMA reads past
 // them return zero, so slots that hold no key are zero in LDS and the
 // 0-probabilities never meet pool contents (NaN * 0 would poison the row).
+//
+// The launch may also hold decode items (the decode tokens of a batch that
+// mixes them with prefill chunks): a work-group given one runs the decode
+// kernel's code (msa_decode_item.h) in this kernel's LDS, so the whole batch
+// is one launch and the bandwidth-bound decode items share the chip with the
+// MFMA-bound chunk items.
 #include "msa_common.h"
+#include "msa_decode_item.h"
 
 namespace msa {
 namespace {
@@ -381,6 +388,14 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
   __shared__ StepTile<D> tile0;
   __shared__ StepTile<D> tile1;
   const WorkItem it = a.items[blockIdx.x];
+  if (it.kind == kDecode) {
+    static_assert(sizeof(dec::DecodeShared<D, 8>) <= sizeof(StepTile<D>), "decode work must fit in one tile");
+    if (it.n_q * a.group <= 4)
+      dec::decode_item<D, 4>(a, it, *reinterpret_cast<dec::DecodeShared<D, 4>*>(&tile0));
+    else
+      dec::decode_item<D, 8>(a, it, *reinterpret_cast<dec::DecodeShared<D, 8>*>(&tile0));
+    return;
+  }
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
