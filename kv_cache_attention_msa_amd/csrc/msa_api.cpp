@@ -424,6 +424,8 @@ int launch_attention(msa_pool* p, const msa_seg_desc* desc, const PlanLayout& L,
   if (!plan.merges.empty()) {
     a.items = nullptr;
     a.n_items = 0;
+    a.max_mrows = 0;
+    for (const MergeItem& m : plan.merges) a.max_mrows = std::max(a.max_mrows, m.n_mrows);
     const int rc = launch(kMerge, [&]() { return launch_merge(a, D, p->desc.dtype, stream); });
     if (rc) return rc;
   }

@@ -9,9 +9,10 @@ namespace {
 using dec::kDecodeThreads;
 
 template <int D, int NM>
-__global__ __launch_bounds__(kDecodeThreads, 2) void msa_decode_kernel(KernelArgs a) {
-  __shared__ dec::DecodeShared<D, NM> sh;
-  dec::decode_item<D, NM>(a, a.items[blockIdx.x], sh);
+__global__ __launch_bounds__(kDecodeThreads, 3) void msa_decode_kernel(KernelArgs a) {
+  __shared__ dec::VRing<D> vr0;
+  __shared__ dec::VRing<D> vr1;
+  dec::decode_item<D, NM>(a, a.items[blockIdx.x], vr0, vr1);
 }
 
 template <int D>

@@ -23,7 +23,10 @@ __global__ __launch_bounds__(256) void msa_merge_kernel(KernelArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = a.group;
   const int ns = mi.n_splits;
-  for (int mr = wave; mr < mi.n_mrows; mr += 4) {
+  // work-group (x, y) merges rows 4 y .. 4 y + 3 of merge item x, one per wave
+  {
+    const int mr = 4 * blockIdx.y + wave;
+    if (mr >= mi.n_mrows) return;
     const int row = mi.q_row0 + mr / g;
     const int head = mi.kv_head * g + mr % g;
     const int pr0 = mi.part_row0 + mr;   // split s of this row: partial row pr0 + s * n_mrows
@@ -46,14 +49,14 @@ __global__ __launch_bounds__(256) void msa_merge_kernel(KernelArgs a) {
         const float* po = a.part_o + (int64_t)(pr0 + s0 * mi.n_mrows) * D + lane * E;
         const int64_t step = (int64_t)mi.n_mrows * D;
         int j = 0;
-        for (; j + 4 <= cnt; j += 4) {
-          float v[4][E];
+        for (; j + 8 <= cnt; j += 8) {
+          float v[8][E];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 8; ++u)
 #pragma unroll
             for (int e = 0; e < E; ++e) v[u][e] = po[(j + u) * step + e];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < 8; ++u) {
             const float wj = __shfl(w, j + u, 64);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[e] += wj > 0.f ? wj * v[u][e] : 0.f;
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) void msa_merge_kernel(KernelArgs a) {
 }
 
 int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream) {
-  dim3 grid(a.n_merges), block(256);
+  dim3 grid(a.n_merges, (a.max_mrows + 3) / 4), block(256);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == MSA_FP32) {
     if (head_dim == 128) hipLaunchKernelGGL((msa_merge_kernel<float, 128>), grid, block, 0, s, a);

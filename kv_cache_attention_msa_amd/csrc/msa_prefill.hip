@@ -389,11 +389,13 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
   __shared__ StepTile<D> tile1;
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kDecode) {
-    static_assert(sizeof(dec::DecodeShared<D, 8>) <= sizeof(StepTile<D>), "decode work must fit in one tile");
+    static_assert(sizeof(dec::VRing<D>) <= sizeof(StepTile<D>), "decode buffers must fit in a tile");
+    dec::VRing<D>& vr0 = *reinterpret_cast<dec::VRing<D>*>(&tile0);
+    dec::VRing<D>& vr1 = *reinterpret_cast<dec::VRing<D>*>(&tile1);
     if (it.n_q * a.group <= 4)
-      dec::decode_item<D, 4>(a, it, *reinterpret_cast<dec::DecodeShared<D, 4>*>(&tile0));
+      dec::decode_item<D, 4>(a, it, vr0, vr1);
     else
-      dec::decode_item<D, 8>(a, it, *reinterpret_cast<dec::DecodeShared<D, 8>*>(&tile0));
+      dec::decode_item<D, 8>(a, it, vr0, vr1);
     return;
   }
   const int t = threadIdx.x;
