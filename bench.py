@@ -547,6 +547,80 @@ def evict_sweep(report=None, sizes=(4000, 5000, 6000, 7000, 8000, 9000, 10000), 
     return rows
 
 
+PHASES = ("QK product issued", "LDS DMA issued", "mask", "softmax", "PV product issued", "metadata + barrier")
+
+
+def phase_trace_run(args):
+    """Per-phase shader clocks of the chunk kernel's steps on the prefill
+    workload, from the measurement build libmsa_trace.so (MSA_PHASE_TRACE:
+    s_memtime between scheduling fences at every phase boundary, summed per
+    work item and wave).  Prints one JSON line; with --report, a summary."""
+    import numpy as np
+    import torch
+    import kv_cache_attention_msa_amd as msa
+    import workloads as W
+    msa.use_library("libmsa_trace.so")
+    wl = W.config2()
+    f, _ = work_of(wl)
+    K, V = wl.dense_pool("cuda")
+    pool = msa.Pool(wl.num_blocks, wl.num_kv_heads, wl.head_dim, msa.BF16, k=K, v=V)
+    q = wl.q.cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(wl.total_q, wl.num_q_heads, dtype=torch.float32, device="cuda")
+    bt = torch.from_numpy(wl.block_table).cuda()
+    desc = msa.SegDesc.from_workload(wl)
+    items, _ = msa.plan_debug(desc, wl.num_kv_heads, wl.head_dim)
+    n_items = int((items["launch"] == msa.KERNEL_PREFILL).sum())
+    trace = torch.zeros(n_items * 4 * 8, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    settle(lambda: msa.forward(q, desc, bt, pool, out, lse, stream))
+    pool.set_option(msa.OPT_TIMING, 1)
+    pool.kernel_time(msa.KERNEL_PREFILL, reset=True)
+    for _ in range(args.steps):
+        msa.forward(q, desc, bt, pool, out, lse, stream)
+    torch.cuda.synchronize()
+    plain_ms, n = pool.kernel_time(msa.KERNEL_PREFILL, reset=True)
+    pool.set_option(msa.OPT_PHASE_TRACE, trace.data_ptr())
+    sums = np.zeros(8)
+    for _ in range(args.steps):
+        trace.zero_()
+        msa.forward(q, desc, bt, pool, out, lse, stream)
+        torch.cuda.synchronize()
+        sums += trace.view(-1, 8).cpu().numpy().astype(np.float64).sum(axis=0)
+    traced_ms, n2 = pool.kernel_time(msa.KERNEL_PREFILL)
+    pool.set_option(msa.OPT_PHASE_TRACE, 0)
+    pool.close()
+    steps = sums[0]
+    per_step = {PHASES[k]: sums[1 + k] / steps for k in range(6)}
+    loop = sums[7] / steps
+    rec = {"workload": wl.name, "build": "libmsa_trace.so (MSA_PHASE_TRACE)",
+           "kernel_us_untraced_calls": plain_ms / n * 1e3, "kernel_us_traced_calls": traced_ms / n2 * 1e3,
+           "wave_steps": int(steps), "clocks_per_step": loop, "phase_clocks_per_step": per_step,
+           "mfma_clocks_per_step_per_simd": 2 * 32 * 32,
+           "mfma_share_of_step": 2 * 32 * 32 / loop,
+           "tflops_untraced": f / (plain_ms / n * 1e-3) / 1e12}
+    print(json.dumps(rec))
+    if args.report:
+        lines = [f"# msa_prefill_kernel on {wl.name}: phase trace", "",
+                 "Commands (from the repository root; the library is built on the build host, then run on an MI355X):",
+                 "", "    python -m kv_cache_attention_msa_amd.csrc.build --phase-trace",
+                 f"    python bench.py --phase-trace --steps {args.steps} --report {args.report}", "",
+                 "The measurement build reads the shader clock (`s_memtime`, between scheduling fences) at every phase",
+                 "boundary of every 64-key step and sums the differences per work item and wave; reading the clock",
+                 "waits for it, so traced steps run longer than plain ones (kernel times below).", "",
+                 f"- kernel time, same build: {rec['kernel_us_untraced_calls']:.1f} us with tracing off, "
+                 f"{rec['kernel_us_traced_calls']:.1f} us with it on ({args.steps} calls each)",
+                 f"- wave-steps traced: {int(steps)} ({args.steps} calls x {n_items} work items x 4 waves x their steps)",
+                 f"- clocks per step and wave: {loop:.0f}; the two waves of a SIMD need 2 x 32 MFMAs x 32 clocks = "
+                 f"2048 MFMA clocks per step, {100 * rec['mfma_share_of_step']:.0f} % of it", "",
+                 "| phase | clocks per step | share |", "|---|---|---|"]
+        for k, v in per_step.items():
+            lines.append(f"| {k} | {v:.0f} | {100 * v / loop:.0f} % |")
+        with open(args.report, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {args.report}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -574,9 +648,14 @@ def main():
     ap.add_argument("--latency-out", help="with --latency-model: also write the full result (JSON) here")
     ap.add_argument("--latency-batch", type=int, default=16, help="requests per step for --latency-model")
     ap.add_argument("--latency-report", help="summarise a --latency-out JSON into --report (no GPU needed)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="per-phase clocks of the chunk kernel (needs libmsa_trace.so: csrc.build --phase-trace)")
     ap.add_argument("--evict-sweep", action="store_true",
                     help="eviction time against 4-10 x 10^3 cached blocks (host only; with --report, a summary)")
     args = ap.parse_args()
+    if args.phase_trace:
+        phase_trace_run(args)
+        return
     if args.latency_report:
         latency_report(args.latency_report, args.report,
                        args.command[0] if args.command else f"python bench.py --latency-model --latency-out {args.latency_report}")

@@ -218,6 +218,15 @@ const char* msa_last_error(void);
                                    enqueued.  Synchronises the stream on every call.
                                    0 (default): ids are clamped into the pool on
                                    the device, without a report                     */
+#define MSA_OPT_PHASE_TRACE 5   /* measurement builds only (libmsa_trace.so, built
+                                   with MSA_PHASE_TRACE): device address of a
+                                   buffer of n_items x 4 x 8 uint64 into which the
+                                   chunk kernel writes, per work item and wave, the
+                                   step count and the summed shader-clock time of
+                                   each phase of its steps (see msa_prefill.hip);
+                                   0 turns it off.  The caller owns the buffer.  A
+                                   library built without tracing returns
+                                   MSA_ERR_UNSUPPORTED for a non-zero value.        */
 
 int msa_pool_set_option(msa_pool* pool, int32_t option, int64_t value);
 

@@ -16,17 +16,18 @@ import numpy as np
 
 __all__ = [
     "MsaError", "Pool", "SegDesc", "forward", "forward_noalloc", "write_kv", "plan_debug", "library_path", "load_library",
+    "use_library",
     "LatencyModel", "latency_fit", "chunk_blocks", "EvictIndex", "lambda_from_lifespan",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
-    "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS", "OPT_CHECK_BLOCK_IDS",
+    "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS", "OPT_CHECK_BLOCK_IDS", "OPT_PHASE_TRACE",
 ]
 
 BF16, FP32 = 0, 1
 SEG_FRESH = 1
 BLOCK_SIZE = 16
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
-OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS, OPT_CHECK_BLOCK_IDS = 1, 2, 3, 4
+OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS, OPT_CHECK_BLOCK_IDS, OPT_PHASE_TRACE = 1, 2, 3, 4, 5
 KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_WRITE = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
@@ -75,10 +76,23 @@ PLAN_ITEM_DTYPE = np.dtype([("kind", "<i4"), ("seq", "<i4"), ("kv_head", "<i4"),
 PLAN_BLOCK_DTYPE = np.dtype([("bt_index", "<i4"), ("pos0", "<i4"), ("valid", "<i4")])
 
 _lib = None
+_lib_name = "libmsa.so"
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _lib_name)
+
+
+def use_library(name: str) -> None:
+    """Select the in-tree library file to load (before the first call):
+    "libmsa.so" (default) or "libmsa_trace.so", the measurement build whose
+    chunk kernel records phase clocks (OPT_PHASE_TRACE)."""
+    global _lib_name
+    if _lib is not None and name != _lib_name:
+        raise RuntimeError(f"{_lib_name} is already loaded")
+    if name not in ("libmsa.so", "libmsa_trace.so"):
+        raise ValueError(f"unknown library {name!r}")
+    _lib_name = name
 
 
 def load_library():

@@ -1,9 +1,13 @@
 """Build libmsa.so (host runtime + gfx950 kernels) in-tree with hipcc.
 
-    python -m kv_cache_attention_msa_amd.csrc.build      # or build() from Python
+    python -m kv_cache_attention_msa_amd.csrc.build                # or build() from Python
+    python -m kv_cache_attention_msa_amd.csrc.build --phase-trace  # measurement build
 
 Every call compiles every source again (objects go to ``_build/`` at the
 repository root, the library to ``kv_cache_attention_msa_amd/libmsa.so``).
+``--phase-trace`` builds ``libmsa_trace.so`` instead: the same library with
+MSA_PHASE_TRACE defined, whose chunk kernel records per-phase clocks
+(``bench.py --phase-trace``); it is never loaded unless asked for.
 """
 from __future__ import annotations
 
@@ -19,6 +23,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
+TRACE_LIB = os.path.join(PKG, "libmsa_trace.so")   # measurement build (MSA_PHASE_TRACE)
 PEAKS_LIB = os.path.join(PKG, "libmsa_peaks.so")   # measurement probes (benchmark only)
 PEAKS_SOURCE = os.path.join(HERE, "peaks", "msa_peaks.hip")
 ARCH = "gfx950"
@@ -51,16 +56,16 @@ def _run(cmd):
     return p.stdout
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def _build_lib(lib: str, objdir: str, defines, verbose: bool, jobs: int) -> None:
+    os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     cmds, objs = [], []
     for src in HOST_SOURCES + HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(objdir, src + ".o")
         extra = DEVICE + ["-x", "hip"] if src.endswith(".hip") else ["-D__HIP_PLATFORM_AMD__"]
         if src in NO_NAN_SOURCES:
             extra = ["-fno-honor-nans"] + extra
-        cmds.append([cc, "-c"] + COMMON + extra + [os.path.join(HERE, src), "-o", obj])
+        cmds.append([cc, "-c"] + COMMON + list(defines) + extra + [os.path.join(HERE, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         outs = list(ex.map(_run, cmds))
@@ -69,9 +74,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             print(" ".join(c))
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_trace(verbose: bool = False, jobs: int = 8) -> str:
+    """The measurement build: libmsa_trace.so with MSA_PHASE_TRACE."""
+    _build_lib(TRACE_LIB, os.path.join(BUILD, "trace"), ["-DMSA_PHASE_TRACE"], verbose, jobs)
+    return TRACE_LIB
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    _build_lib(LIB, BUILD, [], verbose, jobs)
     tmp = PEAKS_LIB + ".tmp"
     _run([cc, "-shared"] + COMMON + DEVICE + ["-x", "hip", PEAKS_SOURCE, "-o", tmp])
     os.replace(tmp, PEAKS_LIB)
@@ -79,4 +96,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--phase-trace" in sys.argv:
+        print(build_trace(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -88,6 +88,7 @@ struct msa_pool {
   // options
   bool timing = false;
   bool check_ids = false;
+  void* trace = nullptr;     // MSA_OPT_PHASE_TRACE buffer (tracing builds)
   int32_t split_blocks = 0;
   int32_t num_cus_override = 0;
 
@@ -404,6 +405,7 @@ int launch_attention(msa_pool* p, const msa_seg_desc* desc, const PlanLayout& L,
   a.causal = desc->causal;
   const float scale = desc->scale != 0.f ? desc->scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.trace = (unsigned long long*)p->trace;
   auto launch = [&](int kind, auto&& fn) -> int {
     if (timed) return timed_launch(p, kind, stream, fn);
     const int e = fn();
@@ -520,6 +522,14 @@ int msa_pool_set_option(msa_pool* p, int32_t option, int64_t value) {
   switch (option) {
     case MSA_OPT_TIMING: p->timing = value != 0; return MSA_OK;
     case MSA_OPT_CHECK_BLOCK_IDS: p->check_ids = value != 0; return MSA_OK;
+    case MSA_OPT_PHASE_TRACE:
+#ifdef MSA_PHASE_TRACE
+      p->trace = (void*)(uintptr_t)value;
+      return MSA_OK;
+#else
+      if (value == 0) return MSA_OK;
+      return set_error(MSA_ERR_UNSUPPORTED, "phase tracing needs the tracing build (libmsa_trace.so)");
+#endif
     case MSA_OPT_SPLIT_BLOCKS:
       if (value < 0 || value > (1 << 30)) return set_error(MSA_ERR_INVALID_ARG, "bad split_blocks");
       p->split_blocks = (int32_t)value;

@@ -114,6 +114,7 @@ struct KernelArgs {
   int32_t causal;
   float scale_log2;       // scale * log2(e)
   int32_t max_mrows;      // largest n_q * group among the launch's items
+  unsigned long long* trace;  // phase clocks of the chunk kernel (tracing builds only), or null
 };
 
 // KV write launch: one wave per (block-list entry, kv head).  Entry e's pos0

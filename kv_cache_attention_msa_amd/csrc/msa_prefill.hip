@@ -316,17 +316,48 @@ struct TileState {
   float m, l;             // per-row reference (log2 domain) and partial row sum
 };
 
+// Phase clocks (measurement builds with MSA_PHASE_TRACE only): the shader
+// clock (s_memtime) is read between scheduling fences at the phase boundaries
+// of every step -- QK product issued, DMA issued, mask, softmax, PV product
+// issued, metadata + barrier -- and summed per phase and wave.  Reading the
+// clock waits for it, so a traced step runs somewhat longer than a plain one.
+#ifdef MSA_PHASE_TRACE
+struct PhaseClock {
+  unsigned long long last = 0, begin = 0;
+  unsigned long long sum[6] = {0, 0, 0, 0, 0, 0};
+  unsigned long long steps = 0;
+};
+__device__ __forceinline__ unsigned long long clock_now() {
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+#define PHASE_START(pc) ((pc).last = clock_now())
+#define PHASE_MARK(pc, k)                             \
+  do {                                                \
+    const unsigned long long t_ = clock_now();        \
+    (pc).sum[k] += t_ - (pc).last;                    \
+    (pc).last = t_;                                   \
+  } while (0)
+#else
+struct PhaseClock {};
+#define PHASE_START(pc) ((void)(pc))
+#define PHASE_MARK(pc, k) ((void)(pc))
+#endif
+
 // One step of 64 keys on tile `tl`; the next step's K and V go into `nx` by
 // DMA meanwhile.  Ends with this wave's DMA complete and a work-group barrier.
 template <int D>
 __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& it, const RowInfo& ri, TileState<D>& st,
                                            const StepTile<D>& tl, StepTile<D>& nx, StepMeta& cur, StepMeta& nxt,
                                            int next_blk, int wave, int lane, const DmaOffsets<D>& dof,
-                                           const uint32_t (&voff)[D / 32]) {
+                                           const uint32_t (&voff)[D / 32], PhaseClock& pc) {
   const int h = lane >> 5;
   const int col = lane & 31;
   const float c2 = a.scale_log2;
 
+  PHASE_START(pc);
   // ---- S^T = K Q^T for 64 keys ----
   f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
 #pragma unroll
@@ -336,9 +367,12 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st.qop[ks], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, st.qop[ks], s1, 0, 0, 0);
   }
+  PHASE_MARK(pc, 0);
 
   dma_step<D>(a, it.kv_head, nxt, nx, wave, dof);
+  PHASE_MARK(pc, 1);
   if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
+  PHASE_MARK(pc, 2);
 
   // ---- online softmax (exp2 domain) ----
   // Probabilities are taken against a per-row reference m instead of the
@@ -362,6 +396,7 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
     rs = exp_half(s0, s1, c2, st.m == kNegInf ? 0.f : st.m, pw);
   }
   st.l += rs;
+  PHASE_MARK(pc, 3);
 
   // ---- O^T += V^T P^T ----
   const char* vb = (const char*)&tl.v[0][0];
@@ -377,10 +412,15 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
       st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pop, st.acc[db], 0, 0, 0);
     }
   }
+  PHASE_MARK(pc, 4);
 
   cur = nxt;
   load_meta(a, next_blk, it.blk_end, it.q_min, nxt);
   __syncthreads();   // waits for this wave's DMA, then for every wave
+  PHASE_MARK(pc, 5);
+#ifdef MSA_PHASE_TRACE
+  pc.steps += 1;
+#endif
 }
 
 template <int D>
@@ -426,6 +466,10 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
     uint32_t voff[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) voff[db] = vtr_offset<D>(lane, db);
+    PhaseClock pc;
+#ifdef MSA_PHASE_TRACE
+    pc.begin = clock_now();
+#endif
     StepMeta cur, nxt;
     load_meta(a, it.blk_begin, it.blk_end, it.q_min, cur);
     dma_step<D>(a, it.kv_head, cur, tile0, wave, dof);
@@ -434,10 +478,20 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
 
     // Unrolled by two so that each step's tiles are known at compile time.
     for (int s = 0; s < nsteps; s += 2) {
-      chunk_step<D>(a, it, ri, st, tile0, tile1, cur, nxt, it.blk_begin + 4 * (s + 2), wave, lane, dof, voff);
+      chunk_step<D>(a, it, ri, st, tile0, tile1, cur, nxt, it.blk_begin + 4 * (s + 2), wave, lane, dof, voff, pc);
       if (s + 1 >= nsteps) break;
-      chunk_step<D>(a, it, ri, st, tile1, tile0, cur, nxt, it.blk_begin + 4 * (s + 3), wave, lane, dof, voff);
+      chunk_step<D>(a, it, ri, st, tile1, tile0, cur, nxt, it.blk_begin + 4 * (s + 3), wave, lane, dof, voff, pc);
     }
+#ifdef MSA_PHASE_TRACE
+    // per item and wave: steps, the six phase sums, the whole loop (clocks)
+    if (a.trace && lane == 0) {
+      unsigned long long* tr = a.trace + ((size_t)blockIdx.x * 4 + wave) * 8;
+      tr[0] = pc.steps;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) tr[1 + k] = pc.sum[k];
+      tr[7] = clock_now() - pc.begin;
+    }
+#endif
   }
 
   // ---- epilogue ----

@@ -136,6 +136,10 @@ def test_pool_creation_checks():
     h = _fake_pool()
     assert lib.msa_pool_set_option(h, msa.OPT_SPLIT_BLOCKS, 4) == 0
     assert lib.msa_pool_set_option(h, 99, 1) == msa.ERR_INVALID_ARG
+    # phase tracing exists only in the measurement build (libmsa_trace.so)
+    assert lib.msa_pool_set_option(h, msa.OPT_PHASE_TRACE, 0x1000) == msa.ERR_UNSUPPORTED
+    assert "tracing build" in lib.msa_last_error().decode()
+    assert lib.msa_pool_set_option(h, msa.OPT_PHASE_TRACE, 0) == 0
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.msa_pool_kernel_time(h, 0, ctypes.byref(ms), ctypes.byref(n), 1) == 0 and n.value == 0
     assert lib.msa_destroy_pool(h) == 0
