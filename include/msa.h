@@ -151,7 +151,9 @@ int msa_forward(const void* q, const msa_seg_desc* desc, const int32_t* block_ta
  * makes no hipMalloc, hipFree, pinned or other device allocation; its plan
  * goes from host memory of the calling thread into the scratch through
  * hipMemcpyAsync on `stream` (a copy from pageable memory, so the call waits
- * until the host side of that copy has been taken).  No kernel timing is
+ * until the host side of that copy has been taken).  Host-side, the planner's
+ * working lists and that per-thread buffer are ordinary heap memory that grows
+ * to the largest call seen and is then reused.  No kernel timing is
  * recorded (MSA_OPT_TIMING is ignored); MSA_OPT_SPLIT_BLOCKS and
  * MSA_OPT_NUM_CUS apply.
  *
