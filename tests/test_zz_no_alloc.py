@@ -1,10 +1,12 @@
 """msa_forward_noalloc: the attention entry point that allocates no device memory.
 
-GPU: called through the C ABI (ctypes, no binding checks in between) twice in
-a row -- the full-size 64-sequence decode workload (split tiles, so the merge
-reads partials from the fixed scratch), then a smaller batch with forced KV
-splits -- each compared bit for bit with msa_forward on the same pool and
-inputs, and element-wise with the fp64 oracle.
+GPU: called through the C ABI (ctypes, no binding checks in between) three
+times in a row -- the full-size 64-sequence decode workload (split tiles, so
+the merge reads partials from the fixed scratch), then a smaller batch with
+forced KV splits, then a small batch of prefill chunks and decode tokens (one
+fused launch, forced splits on both kinds) -- each compared bit for bit with
+msa_forward on the same pool and inputs, and element-wise with the fp64
+oracle.
 CPU: a call whose plan exceeds the fixed scratch is refused before any HIP
 call.
 """
@@ -54,8 +56,11 @@ def _run_pair(wl, split_blocks):
 def test_noalloc_matches_forward_twice_second_smaller():
     big = W.config3()
     small = W.random_case(81, batch=2, H_q=8, H_kv=2, d=128, max_ctx=500, max_chunk=60)
+    mixed = W.custom([([(0, 256), (300, 64)], list(range(300, 364))), ([(0, 200)], [199]), ([(16, 500)], [515]),
+                      ([(0, 90), (120, 33)], [152])], H_q=8, H_kv=2, d=128, seed=83, name="mixed_small")
     _run_pair(big, split_blocks=0)       # automatic splits: decode partials + merge in the scratch
-    _run_pair(small, split_blocks=3)     # forced splits on chunk and decode items
+    _run_pair(small, split_blocks=3)     # forced splits on chunk items
+    _run_pair(mixed, split_blocks=3)     # decode items inside the chunk launch, both kinds split
 
 
 def test_noalloc_refuses_plans_beyond_the_scratch():
