@@ -315,6 +315,49 @@ def cpu_baseline(wl, flops_per_row, budget_s=12.0):
             "blas_threads_requested": BLAS_THREADS}
 
 
+def cpu_oracle_configs(budget_s=6.0, row_block=256):
+    """The fp64 oracle beside the other benchmark workloads (decode, heavy
+    fragmentation, mixed batch), each on a bounded sample: query rows in
+    order, in blocks of at most row_block rows of one sequence, until about
+    budget_s of CPU time.  Rates in each workload's own unit: GB/s of
+    algorithmic bytes for decode (whole sequences of one token), TFLOP/s of
+    algorithmic FLOPs otherwise.  Context only."""
+    import numpy as np
+    import workloads as W
+    from oracle import attend
+    out = {}
+    for wl, unit in ((W.config3(), "GB/s"), (W.config4(), "TFLOP/s"), (W.config5(), "TFLOP/s")):
+        Kp, Vp = wl.sparse_pools_f64()
+        q64 = wl.q_f64()
+        counts, _ = visible_counts(wl)
+        t, rows_done, flops, seqs = 0.0, 0, 0.0, []
+        for b in range(wl.batch):
+            r0, r1 = int(wl.q_offsets[b]), int(wl.q_offsets[b + 1])
+            for c0 in range(r0, r1, row_block):
+                rows = np.arange(c0, min(r1, c0 + row_block))
+                t0 = time.perf_counter()
+                attend(q64, wl.q_offsets, wl.q_pos, wl.seg_offsets, wl.segs, wl.block_table, Kp, Vp,
+                       wl.num_kv_heads, scale=wl.scale, causal=bool(wl.causal), rows=rows)
+                t += time.perf_counter() - t0
+                rows_done += len(rows)
+                flops += float(counts[rows].sum()) * wl.num_q_heads * 4 * wl.head_dim
+                if t >= budget_s:
+                    break
+            seqs.append(b)
+            if t >= budget_s:
+                break
+        if unit == "GB/s":
+            _, nb = work_of(W.subset(wl, seqs, wl.name + "_sample"))
+            value = nb / t / 1e9
+        else:
+            value = flops / t / 1e12
+        out[wl.name] = {"value": value, "unit": unit,
+                        "sample": f"{rows_done} query rows of the first {len(seqs)} of {wl.batch} sequences "
+                                  f"(all heads, all visible keys), fp64 numpy, {t:.1f} s"}
+        del Kp, Vp, q64
+    return out
+
+
 # ---------------------------------------------------------------------------
 # profiler helpers
 # ---------------------------------------------------------------------------
@@ -735,6 +778,8 @@ def main():
         sr["frac_of_attainable"] = sr["achieved"] / att[ref] if sr.get("achieved") else None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, counts * wl.num_q_heads * 4 * wl.head_dim)
+        if not args.no_secondary:
+            line["cpu_baseline"]["other_workloads"] = cpu_oracle_configs()
     print(json.dumps(line), flush=True)
 
 
