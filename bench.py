@@ -614,7 +614,7 @@ def phase_trace_run(args):
     desc = msa.SegDesc.from_workload(wl)
     items, _ = msa.plan_debug(desc, wl.num_kv_heads, wl.head_dim)
     n_items = int((items["launch"] == msa.KERNEL_PREFILL).sum())
-    trace = torch.zeros(n_items * 4 * 8, dtype=torch.int64, device="cuda")
+    trace = torch.zeros(n_items * 8 * 8, dtype=torch.int64, device="cuda")   # 8 wave slots per item
     stream = torch.cuda.current_stream()
     settle(lambda: msa.forward(q, desc, bt, pool, out, lse, stream))
     pool.set_option(msa.OPT_TIMING, 1)
@@ -653,7 +653,8 @@ def phase_trace_run(args):
                  "waits for it, so traced steps run longer than plain ones (kernel times below).", "",
                  f"- kernel time, same build: {rec['kernel_us_untraced_calls']:.1f} us with tracing off, "
                  f"{rec['kernel_us_traced_calls']:.1f} us with it on ({args.steps} calls each)",
-                 f"- wave-steps traced: {int(steps)} ({args.steps} calls x {n_items} work items x 4 waves x their steps)",
+                 f"- wave-steps traced: {int(steps)} ({args.steps} calls x {n_items} work items x their waves x their "
+                 f"steps)",
                  f"- clocks per step and wave: {loop:.0f}; the two waves of a SIMD need 2 x 32 MFMAs x 32 clocks = "
                  f"2048 MFMA clocks per step, {100 * rec['mfma_share_of_step']:.0f} % of it", "",
                  "| phase | clocks per step | share |", "|---|---|---|"]

@@ -222,7 +222,9 @@ const char* msa_last_error(void);
                                    the device, without a report                     */
 #define MSA_OPT_PHASE_TRACE 5   /* measurement builds only (libmsa_trace.so, built
                                    with MSA_PHASE_TRACE): device address of a
-                                   buffer of n_items x 4 x 8 uint64 into which the
+                                   buffer of n_items x 8 x 8 uint64 (8 wave slots
+                                   per work item of the chunk launch, zeroed by the
+                                   caller) into which the
                                    chunk kernel writes, per work item and wave, the
                                    step count and the summed shader-clock time of
                                    each phase of its steps (see msa_prefill.hip);

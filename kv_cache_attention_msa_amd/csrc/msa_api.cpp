@@ -417,7 +417,7 @@ int launch_attention(msa_pool* p, const msa_seg_desc* desc, const PlanLayout& L,
     a.n_items = (int32_t)plan.items[k].size();
     a.max_mrows = plan.max_mrows[k];
     const int rc = launch(k, [&]() {
-      if (k == kPrefill) return launch_prefill(a, D, stream);
+      if (k == kPrefill) return launch_prefill(a, D, plan.chunk_waves, stream);
       if (k == kDecode) return launch_decode(a, D, stream);
       return launch_fp32(a, D, stream);
     });

@@ -300,5 +300,13 @@ __device__ __forceinline__ void decode_item(const KernelArgs& a, const WorkItem&
   }
 }
 
+// For the waves of a larger work-group that take no part in its decode item:
+// the work-group barriers decode_item executes (exactly two, both after its
+// block loop), so that every wave of the work-group reaches each of them.
+__device__ __forceinline__ void decode_item_idle() {
+  __syncthreads();
+  __syncthreads();
+}
+
 }  // namespace dec
 }  // namespace msa

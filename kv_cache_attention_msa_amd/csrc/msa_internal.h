@@ -11,7 +11,8 @@
 namespace msa {
 
 constexpr int kBlock = MSA_BLOCK_SIZE;
-constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per prefill tile
+constexpr int kPrefillMRows = 128;   // (query row, head-in-group) pairs per prefill tile (4 waves)
+constexpr int kPrefillMRowsWide = 256;  // the same with 8-wave work-groups (long-context launches)
 constexpr int kDecodeMRows = 8;      // pairs per decode tile (at most 8 of the 16 MFMA columns)
 constexpr int kFp32MRows = 16;       // pairs per fp32 tile (one wave each)
 constexpr int kMaxGroup = 128;       // largest q-heads-per-kv-head ratio accepted
@@ -78,6 +79,10 @@ struct Plan {
   int64_t part_rows = 0;            // partial rows (each head_dim floats + 1 lse)
   int32_t max_mrows[3] = {0, 0, 0}; // largest (query row, head) count of an item, per kind
   int32_t total_q = 0;
+  // Waves per work-group of the chunk launch: 4 (128-row tiles, two
+  // work-groups per CU) or 8 (256-row tiles, one per CU: half the K/V
+  // staging per FLOP, for launches with at least two such tiles per CU).
+  int32_t chunk_waves = 4;
 };
 
 struct PlanConfig {
@@ -135,7 +140,7 @@ struct WriteArgs {
 int scratch_address(int device, void** ptr, std::string& err);
 
 // Launchers (one per kernel source).  Return a hipError_t value.
-int launch_prefill(const KernelArgs& a, int head_dim, void* stream);
+int launch_prefill(const KernelArgs& a, int head_dim, int waves, void* stream);
 int launch_decode(const KernelArgs& a, int head_dim, void* stream);
 int launch_fp32(const KernelArgs& a, int head_dim, void* stream);
 int launch_merge(const KernelArgs& a, int head_dim, int dtype, void* stream);

@@ -40,13 +40,13 @@ struct Tile {
 };
 
 // Largest block-count of one work item before the planner splits a tile.
-int64_t auto_chunk(int kind, int64_t total_blocks, int num_cus) {
+int64_t auto_chunk(int kind, int64_t total_blocks, int num_cus, int chunk_waves) {
   // Work-groups per compute unit the planner balances for: the chunk kernel
-  // holds two per CU; the decode kernel holds three, and two items per
-  // resident slot keep the bandwidth-bound launch busy to its end (measured:
-  // 8 decode tokens over 2k-16k contexts 56.8 -> 52.1 us against one item per
-  // slot, 64 tokens over 1k-8k unchanged).
-  const int64_t slots_per_cu = (kind == kPrefill) ? 2 : (kind == kDecode ? 6 : 4);
+  // holds two per CU (one with 8-wave work-groups); the decode kernel holds
+  // three, and two items per resident slot keep the bandwidth-bound launch
+  // busy to its end (measured: 8 decode tokens over 2k-16k contexts 56.8 ->
+  // 52.1 us against one item per slot, 64 tokens over 1k-8k unchanged).
+  const int64_t slots_per_cu = (kind == kPrefill) ? (chunk_waves == 8 ? 1 : 2) : (kind == kDecode ? 6 : 4);
   const int64_t min_chunk = (kind == kPrefill) ? 16 : (kind == kDecode ? 32 : 4);
   const int64_t slots = std::max<int64_t>(1, slots_per_cu * num_cus);
   return std::max<int64_t>(min_chunk, (total_blocks + slots - 1) / slots);
@@ -158,6 +158,23 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   // resize() keeps the entries of an earlier call; every one is rewritten below
   plan.blocks.resize((size_t)n_blocks);
 
+  // Chunk work-group size: 8 waves (256-row tiles) when the chunk tiles of
+  // that size give at least two per compute unit, else 4 (128-row tiles).  A
+  // long-context launch then stages each K/V block into half as many
+  // work-groups (the heavy-fragmentation workload, 2 x 32k context: 2.02 ->
+  // 1.93 ms); a short one keeps enough tiles to fill the chip.
+  plan.chunk_waves = 4;
+  if (cfg.dtype == MSA_BF16) {
+    int64_t wide_tiles = 0;
+    const int32_t wide_rows = std::max(1, kPrefillMRowsWide / group);
+    for (int b = 0; b < B; ++b) {
+      const int32_t nq = d->q_offsets[b + 1] - d->q_offsets[b];
+      const bool decode = group <= kDecodeMRows && (int64_t)nq * group <= kDecodeMRows;
+      if (nq > 0 && !decode) wide_tiles += (nq + wide_rows - 1) / wide_rows;
+    }
+    if (wide_tiles * cfg.num_kv_heads >= 2 * (int64_t)cfg.num_cus) plan.chunk_waves = 8;
+  }
+
   std::vector<Tile>& tiles = plan_tiles();
   std::vector<int32_t>& order = plan_order();
   tiles.clear();
@@ -215,7 +232,7 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
       tile_rows = nq;
     } else {
       kind = kPrefill;
-      tile_rows = kPrefillMRows / group;
+      tile_rows = std::max(1, (plan.chunk_waves == 8 ? kPrefillMRowsWide : kPrefillMRows) / group);
     }
     for (int32_t r = q0; r < q1; r += tile_rows) {
       const int32_t n = std::min(tile_rows, q1 - r);
@@ -252,7 +269,7 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   for (const Tile& t : tiles) total_blocks[t.launch] += (int64_t)(t.blk_end - t.blk_begin) * cfg.num_kv_heads;
   int64_t chunk[3];
   for (int k = 0; k < 3; ++k)
-    chunk[k] = cfg.split_blocks > 0 ? cfg.split_blocks : auto_chunk(k, total_blocks[k], cfg.num_cus);
+    chunk[k] = cfg.split_blocks > 0 ? cfg.split_blocks : auto_chunk(k, total_blocks[k], cfg.num_cus, plan.chunk_waves);
 
   // Split count of every tile, then the item and merge counts, so that the
   // lists are sized once and written in place.

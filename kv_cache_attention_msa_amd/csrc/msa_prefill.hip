@@ -1,10 +1,13 @@
 // Chunk (prefill) kernel for bf16 pools: exact softmax attention of a tile of
-// 128 (query row, q head) pairs against a run of KV blocks, with both matrix
-// products on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
+// 128 or 256 (query row, q head) pairs against a run of KV blocks, with both
+// matrix products on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulate).
 //
-// Work-group: 4 waves; wave w owns tile rows 32w..32w+31; two work-groups
-// share a CU.  A tile row is a (query row, head of the kv head's GQA group)
-// pair, so the K/V tile staged in LDS serves every q head of the group.
+// Work-group: W = 4 waves (two work-groups per CU) or W = 8 (one per CU, for
+// launches with enough tiles: each K/V block is staged into half as many
+// work-groups); wave w owns tile rows 32w..32w+31.  A tile row is a (query
+// row, head of the kv head's GQA group) pair, so the K/V tile staged in LDS
+// serves every q head of the group.
 //
 // Per step of 64 keys (4 pool blocks of the position-ordered block list, which
 // may span segment boundaries):
@@ -43,7 +46,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr int kStepKeys = 64;   // keys per step = 4 blocks
 constexpr float kRefSumLimit = 1048576.f;  // 2^20: largest accepted partial row sum per step
 
@@ -166,25 +168,31 @@ __device__ __forceinline__ DmaOffsets<D> dma_offsets(int lane) {
   return o;
 }
 
-// One step's K and V of block `wave` (each wave moves one of the 4 blocks)
-// from the pool into a tile by LDS DMA.
-template <int D>
+// One step's K and V from the pool into a tile by LDS DMA: with 4 waves,
+// wave w moves K and V of block w; with 8, waves 0-3 move K and waves 4-7 V of
+// block w % 4.
+template <int D, int W>
 __device__ __forceinline__ void dma_step(const KernelArgs& a, int kv_head, const StepMeta& m, StepTile<D>& tl,
                                          int wave, const DmaOffsets<D>& o) {
   constexpr int CPR = D / 8;
   constexpr int RPI = 64 / CPR;
-  const int phys = m.phys(wave), valid = m.valid(wave);
-  const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(a.k, kv_head, a.num_kv_heads, phys, valid);
-  const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(a.v, kv_head, a.num_kv_heads, phys, valid);
+  const int b = wave & 3;
+  const int phys = m.phys(b), valid = m.valid(b);
+  if (W == 4 || wave < 4) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(a.k, kv_head, a.num_kv_heads, phys, valid);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int off = (int)o.k[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&tl.k[16 * wave + i * RPI][0], 16, off, 0, 0, 0);
+    for (int i = 0; i < D / 32; ++i) {
+      const int off = (int)o.k[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&tl.k[16 * b + i * RPI][0], 16, off, 0, 0, 0);
+    }
   }
+  if (W == 4 || wave >= 4) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(a.v, kv_head, a.num_kv_heads, phys, valid);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int off = (int)o.v + i * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&tl.v[16 * wave + i * RPI][0], 16, off, 0, 0, 0);
+    for (int i = 0; i < D / 32; ++i) {
+      const int off = (int)o.v + i * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&tl.v[16 * b + i * RPI][0], 16, off, 0, 0, 0);
+    }
   }
 }
 
@@ -348,7 +356,7 @@ struct PhaseClock {};
 
 // One step of 64 keys on tile `tl`; the next step's K and V go into `nx` by
 // DMA meanwhile.  Ends with this wave's DMA complete and a work-group barrier.
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& it, const RowInfo& ri, TileState<D>& st,
                                            const StepTile<D>& tl, StepTile<D>& nx, StepMeta& cur, StepMeta& nxt,
                                            int next_blk, int wave, int lane, const DmaOffsets<D>& dof,
@@ -369,7 +377,7 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
   }
   PHASE_MARK(pc, 0);
 
-  dma_step<D>(a, it.kv_head, nxt, nx, wave, dof);
+  dma_step<D, W>(a, it.kv_head, nxt, nx, wave, dof);
   PHASE_MARK(pc, 1);
   if (!cur.full) mask_half(s0, s1, cur, h, ri.qpos, a.causal);
   PHASE_MARK(pc, 2);
@@ -423,13 +431,19 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
 #endif
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) {
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void msa_prefill_kernel(KernelArgs a) {
   __shared__ StepTile<D> tile0;
   __shared__ StepTile<D> tile1;
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kDecode) {
     static_assert(sizeof(dec::VRing<D>) <= sizeof(StepTile<D>), "decode buffers must fit in a tile");
+    // the decode code runs on 4 waves; the others of an 8-wave work-group
+    // only take part in its barriers
+    if (W == 8 && threadIdx.x >= dec::kDecodeThreads) {
+      dec::decode_item_idle();
+      return;
+    }
     dec::VRing<D>& vr0 = *reinterpret_cast<dec::VRing<D>*>(&tile0);
     dec::VRing<D>& vr1 = *reinterpret_cast<dec::VRing<D>*>(&tile1);
     if (it.n_q * a.group <= 4)
@@ -472,20 +486,21 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
 #endif
     StepMeta cur, nxt;
     load_meta(a, it.blk_begin, it.blk_end, it.q_min, cur);
-    dma_step<D>(a, it.kv_head, cur, tile0, wave, dof);
+    dma_step<D, W>(a, it.kv_head, cur, tile0, wave, dof);
     load_meta(a, it.blk_begin + 4, it.blk_end, it.q_min, nxt);
     __syncthreads();
 
     // Unrolled by two so that each step's tiles are known at compile time.
     for (int s = 0; s < nsteps; s += 2) {
-      chunk_step<D>(a, it, ri, st, tile0, tile1, cur, nxt, it.blk_begin + 4 * (s + 2), wave, lane, dof, voff, pc);
+      chunk_step<D, W>(a, it, ri, st, tile0, tile1, cur, nxt, it.blk_begin + 4 * (s + 2), wave, lane, dof, voff, pc);
       if (s + 1 >= nsteps) break;
-      chunk_step<D>(a, it, ri, st, tile1, tile0, cur, nxt, it.blk_begin + 4 * (s + 3), wave, lane, dof, voff, pc);
+      chunk_step<D, W>(a, it, ri, st, tile1, tile0, cur, nxt, it.blk_begin + 4 * (s + 3), wave, lane, dof, voff, pc);
     }
 #ifdef MSA_PHASE_TRACE
-    // per item and wave: steps, the six phase sums, the whole loop (clocks)
+    // per item and wave (8 slots per item, whatever W): steps, the six phase
+    // sums, the whole loop (clocks)
     if (a.trace && lane == 0) {
-      unsigned long long* tr = a.trace + ((size_t)blockIdx.x * 4 + wave) * 8;
+      unsigned long long* tr = a.trace + ((size_t)blockIdx.x * 8 + wave) * 8;
       tr[0] = pc.steps;
 #pragma unroll
       for (int k = 0; k < 6; ++k) tr[1 + k] = pc.sum[k];
@@ -500,12 +515,17 @@ __global__ __launch_bounds__(kThreads, 2) void msa_prefill_kernel(KernelArgs a) 
 
 }  // namespace
 
-int launch_prefill(const KernelArgs& a, int head_dim, void* stream) {
-  dim3 grid(a.n_items), block(kThreads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(msa_prefill_kernel<128>, grid, block, 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL(msa_prefill_kernel<64>, grid, block, 0, (hipStream_t)stream, a);
+int launch_prefill(const KernelArgs& a, int head_dim, int waves, void* stream) {
+  const dim3 grid(a.n_items), block(64 * waves);
+  const hipStream_t st = (hipStream_t)stream;
+  if (waves != 4 && waves != 8) return (int)hipErrorInvalidValue;
+  if (head_dim == 128) {
+    if (waves == 8) hipLaunchKernelGGL((msa_prefill_kernel<128, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((msa_prefill_kernel<128, 4>), grid, block, 0, st, a);
+  } else {
+    if (waves == 8) hipLaunchKernelGGL((msa_prefill_kernel<64, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((msa_prefill_kernel<64, 4>), grid, block, 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 
