@@ -220,6 +220,11 @@ const char* msa_last_error(void);
                                    enqueued.  Synchronises the stream on every call.
                                    0 (default): ids are clamped into the pool on
                                    the device, without a report                     */
+#define MSA_OPT_CHUNK_WAVES 6   /* 4 or 8: work-group size (waves) of the bf16 chunk
+                                   launch, 128- or 256-row tiles; 0 (default): the
+                                   planner's choice (8 only for prefill-only batches
+                                   with at least two 256-row tiles per compute unit
+                                   and long contexts)                                */
 #define MSA_OPT_PHASE_TRACE 5   /* measurement builds only (libmsa_trace.so, built
                                    with MSA_PHASE_TRACE): device address of a
                                    buffer of n_items x 8 x 8 uint64 (8 wave slots

@@ -20,14 +20,14 @@ __all__ = [
     "LatencyModel", "latency_fit", "chunk_blocks", "EvictIndex", "lambda_from_lifespan",
     "BF16", "FP32", "SEG_FRESH", "BLOCK_SIZE", "EXPORTED_SYMBOLS",
     "KERNEL_PREFILL", "KERNEL_DECODE", "KERNEL_FP32", "KERNEL_MERGE", "KERNEL_UPLOAD", "KERNEL_WRITE",
-    "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS", "OPT_CHECK_BLOCK_IDS", "OPT_PHASE_TRACE",
+    "OPT_TIMING", "OPT_SPLIT_BLOCKS", "OPT_NUM_CUS", "OPT_CHECK_BLOCK_IDS", "OPT_PHASE_TRACE", "OPT_CHUNK_WAVES",
 ]
 
 BF16, FP32 = 0, 1
 SEG_FRESH = 1
 BLOCK_SIZE = 16
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
-OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS, OPT_CHECK_BLOCK_IDS, OPT_PHASE_TRACE = 1, 2, 3, 4, 5
+OPT_TIMING, OPT_SPLIT_BLOCKS, OPT_NUM_CUS, OPT_CHECK_BLOCK_IDS, OPT_PHASE_TRACE, OPT_CHUNK_WAVES = 1, 2, 3, 4, 5, 6
 KERNEL_PREFILL, KERNEL_DECODE, KERNEL_FP32, KERNEL_MERGE, KERNEL_UPLOAD, KERNEL_WRITE = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (

@@ -91,6 +91,7 @@ struct msa_pool {
   void* trace = nullptr;     // MSA_OPT_PHASE_TRACE buffer (tracing builds)
   int32_t split_blocks = 0;
   int32_t num_cus_override = 0;
+  int32_t chunk_waves = 0;   // MSA_OPT_CHUNK_WAVES
 
   // Plan upload: call n packs its plan into pinned, device-mapped staging
   // buffer n % kSlots; a small kernel on the caller's stream copies it into the
@@ -276,6 +277,7 @@ int prepare_call(msa_pool* p, const msa_seg_desc* desc, const void* q, const int
   cfg.dtype = p->desc.dtype;
   cfg.num_cus = p->num_cus_override > 0 ? p->num_cus_override : (p->num_cus > 0 ? p->num_cus : 256);
   cfg.split_blocks = p->split_blocks;
+  cfg.chunk_waves = p->chunk_waves;
   std::string err;
   int rc = build_plan(desc, cfg, p->plan, err);
   if (rc) return set_error(rc, "%s", err.c_str());
@@ -303,6 +305,7 @@ int refresh_cus(msa_pool* p, const msa_seg_desc* desc) {
     cfg.dtype = p->desc.dtype;
     cfg.num_cus = p->num_cus;
     cfg.split_blocks = p->split_blocks;
+    cfg.chunk_waves = p->chunk_waves;
     std::string err;
     int rc = build_plan(desc, cfg, p->plan, err);
     if (rc) return set_error(rc, "%s", err.c_str());
@@ -533,6 +536,10 @@ int msa_pool_set_option(msa_pool* p, int32_t option, int64_t value) {
     case MSA_OPT_SPLIT_BLOCKS:
       if (value < 0 || value > (1 << 30)) return set_error(MSA_ERR_INVALID_ARG, "bad split_blocks");
       p->split_blocks = (int32_t)value;
+      return MSA_OK;
+    case MSA_OPT_CHUNK_WAVES:
+      if (value != 0 && value != 4 && value != 8) return set_error(MSA_ERR_INVALID_ARG, "chunk waves must be 0, 4 or 8");
+      p->chunk_waves = (int32_t)value;
       return MSA_OK;
     case MSA_OPT_NUM_CUS:
       if (value < 0 || value > 65536) return set_error(MSA_ERR_INVALID_ARG, "bad num_cus");

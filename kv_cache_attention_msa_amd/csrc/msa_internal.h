@@ -91,6 +91,7 @@ struct PlanConfig {
   int32_t dtype = MSA_BF16;
   int32_t num_cus = 256;
   int32_t split_blocks = 0;         // >0 forces this cap on blocks per item
+  int32_t chunk_waves = 0;          // 4 or 8 forces the chunk work-group size; 0: the planner's choice
 };
 
 // Checks every argument of the descriptor and builds the plan.  Host only;

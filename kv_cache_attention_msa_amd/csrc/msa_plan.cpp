@@ -158,21 +158,38 @@ int build_plan(const msa_seg_desc* d, const PlanConfig& cfg, Plan& plan, std::st
   // resize() keeps the entries of an earlier call; every one is rewritten below
   plan.blocks.resize((size_t)n_blocks);
 
-  // Chunk work-group size: 8 waves (256-row tiles) when the chunk tiles of
-  // that size give at least two per compute unit, else 4 (128-row tiles).  A
-  // long-context launch then stages each K/V block into half as many
-  // work-groups (the heavy-fragmentation workload, 2 x 32k context: 2.02 ->
-  // 1.93 ms); a short one keeps enough tiles to fill the chip.
+  // Chunk work-group size: 8 waves (256-row tiles, one work-group per CU)
+  // for a batch of prefill chunks only, whose 256-row tiles number at least
+  // two per compute unit and whose contexts average at least 8 MiB of K/V per
+  // kv head (twice an XCD's L2): each K/V block is then staged into half as
+  // many work-groups, and those re-reads would otherwise go past the L2 (the
+  // heavy-fragmentation workload, 2 x 32k context: 1.97 -> 1.92 ms).  Else 4
+  // waves (128-row tiles, two per CU): shorter contexts stay in the L2, and
+  // a decode item would leave half of an 8-wave work-group idle (both measured
+  // slower with 8 waves).
   plan.chunk_waves = 4;
   if (cfg.dtype == MSA_BF16) {
-    int64_t wide_tiles = 0;
     const int32_t wide_rows = std::max(1, kPrefillMRowsWide / group);
+    int64_t wide_tiles = 0, tile_blocks = 0;
+    bool any_decode_seq = false;
     for (int b = 0; b < B; ++b) {
       const int32_t nq = d->q_offsets[b + 1] - d->q_offsets[b];
-      const bool decode = group <= kDecodeMRows && (int64_t)nq * group <= kDecodeMRows;
-      if (nq > 0 && !decode) wide_tiles += (nq + wide_rows - 1) / wide_rows;
+      if (nq == 0) continue;
+      if (group <= kDecodeMRows && (int64_t)nq * group <= kDecodeMRows) {
+        any_decode_seq = true;
+        continue;
+      }
+      int64_t nblk = 0;
+      for (int32_t sg = d->seg_offsets[b]; sg < d->seg_offsets[b + 1]; ++sg) nblk += (d->segs[sg].len + kBlock - 1) / kBlock;
+      const int64_t t = (nq + wide_rows - 1) / wide_rows;
+      wide_tiles += t;
+      tile_blocks += t * nblk;
     }
-    if (wide_tiles * cfg.num_kv_heads >= 2 * (int64_t)cfg.num_cus) plan.chunk_waves = 8;
+    const int64_t block_bytes = (int64_t)kBlock * cfg.head_dim * 2 * 2;   // K and V of one block, one kv head
+    if (!any_decode_seq && wide_tiles * cfg.num_kv_heads >= 2 * (int64_t)cfg.num_cus &&
+        tile_blocks * block_bytes >= wide_tiles * (int64_t(8) << 20))
+      plan.chunk_waves = 8;
+    if (cfg.chunk_waves == 4 || cfg.chunk_waves == 8) plan.chunk_waves = cfg.chunk_waves;
   }
 
   std::vector<Tile>& tiles = plan_tiles();

@@ -26,9 +26,9 @@ class GpuCase:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(wl.total_q, wl.num_q_heads, dtype=torch.float32, device=device)
 
-    def run(self, split_blocks=0, sync=True, num_cus=0):
+    def run(self, split_blocks=0, sync=True, chunk_waves=0):
         self.pool.set_option(msa.OPT_SPLIT_BLOCKS, split_blocks)
-        self.pool.set_option(msa.OPT_NUM_CUS, num_cus)
+        self.pool.set_option(msa.OPT_CHUNK_WAVES, chunk_waves)
         self.out.fill_(float("nan"))
         self.lse.fill_(float("nan"))
         msa.forward(self.q, self.desc, self.bt, self.pool, self.out, self.lse)

@@ -17,11 +17,11 @@ from msa_gpu_util import GpuCase, compare, oracle_result
 pytestmark = pytest.mark.gpu
 
 
-def _check(wl, split_blocks=0, rows=None, num_cus=0):
-    print(f"[parity] {wl.name} split_blocks={split_blocks} num_cus={num_cus}", flush=True)
+def _check(wl, split_blocks=0, rows=None, chunk_waves=0):
+    print(f"[parity] {wl.name} split_blocks={split_blocks} chunk_waves={chunk_waves}", flush=True)
     case = GpuCase(wl)
     try:
-        out, lse = case.run(split_blocks, num_cus=num_cus)
+        out, lse = case.run(split_blocks, chunk_waves=chunk_waves)
     finally:
         case.close()
     ref_out, ref_lse = oracle_result(wl, rows)
@@ -52,15 +52,17 @@ def test_random_bf16_forced_split(seed):
 
 @pytest.mark.parametrize("seed", range(4))
 def test_random_bf16_eight_wave_chunk(seed):
-    """Planning for one compute unit makes every chunk launch take 8-wave
-    work-groups (256-row tiles); the decode items of these mixed batches then
-    run on half of each work-group while the other waves only join its
-    barriers."""
+    """The chunk launch forced to 8-wave work-groups (256-row tiles) on small
+    mixed batches: the decode items then run on half of each work-group while
+    the other waves only join its barriers.  (By itself the planner takes 8
+    waves only for long-context prefill-only batches, e.g. the heavy-
+    fragmentation workload of the full-size test.)"""
     H = [(8, 2), (32, 8), (64, 8), (6, 2)][seed]
     d = 128 if seed % 2 == 0 else 64
     wl = W.random_case(60 + seed, batch=4, H_q=H[0], H_kv=H[1], d=d, max_ctx=700, max_chunk=300)
-    _check(wl, num_cus=1)
-    _check(wl, split_blocks=3, num_cus=1)
+    _check(wl, chunk_waves=8)
+    _check(wl, split_blocks=3, chunk_waves=8)
+    _check(wl, chunk_waves=4)
 
 
 def test_random_fp32_cases():

@@ -140,6 +140,8 @@ def test_pool_creation_checks():
     assert lib.msa_pool_set_option(h, msa.OPT_PHASE_TRACE, 0x1000) == msa.ERR_UNSUPPORTED
     assert "tracing build" in lib.msa_last_error().decode()
     assert lib.msa_pool_set_option(h, msa.OPT_PHASE_TRACE, 0) == 0
+    for w, code in ((0, 0), (4, 0), (8, 0), (5, msa.ERR_INVALID_ARG), (16, msa.ERR_INVALID_ARG)):
+        assert lib.msa_pool_set_option(h, msa.OPT_CHUNK_WAVES, w) == code
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.msa_pool_kernel_time(h, 0, ctypes.byref(ms), ctypes.byref(n), 1) == 0 and n.value == 0
     assert lib.msa_destroy_pool(h) == 0
@@ -367,3 +369,15 @@ def test_binding_checks_tensor_shapes_before_the_library():
         msa.forward(0x1000, d, 0x2000, pool, 0x3000, torch.zeros(3, 5))
     with pytest.raises(ValueError, match="block_table must be"):
         msa.forward(0x1000, d, torch.zeros(1, dtype=torch.int64), pool, 0x3000)
+
+
+def test_chunk_work_group_size_choice():
+    """The planner takes 8-wave work-groups (256-row tiles) only for a
+    prefill-only batch with at least two such tiles per compute unit and long
+    contexts: the heavy-fragmentation workload; the prefill and mixed
+    workloads keep 128-row tiles."""
+    for wl, rows in ((W.config2(), 128), (W.config4(), 256), (W.config5(), 128)):
+        group = wl.num_q_heads // wl.num_kv_heads
+        items, _ = msa.plan_debug(msa.SegDesc.from_workload(wl), wl.num_kv_heads, wl.head_dim)
+        chunk = items[items["launch"] == msa.KERNEL_PREFILL]
+        assert int((chunk["n_q"] * group).max()) == rows, wl.name
