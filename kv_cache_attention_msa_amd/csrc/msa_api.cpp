@@ -419,6 +419,7 @@ int launch_attention(msa_pool* p, const msa_seg_desc* desc, const PlanLayout& L,
     a.items = (const WorkItem*)(dplan + L.off_items[k]);
     a.n_items = (int32_t)plan.items[k].size();
     a.max_mrows = plan.max_mrows[k];
+    a.stream_kv = plan.stream_kv[k];
     const int rc = launch(k, [&]() {
       if (k == kPrefill) return launch_prefill(a, D, plan.chunk_waves, stream);
       if (k == kDecode) return launch_decode(a, D, stream);

@@ -127,10 +127,17 @@ __device__ __forceinline__ void dma_v(const KernelArgs& a, int kv_head, const Bl
   constexpr int RPI = 64 / (D / 8);
   const char* p = (const char*)a.v + ((int64_t)b.phys * a.num_kv_heads + kv_head) * (kBlock * D * 2);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, b.valid * D * 2, 0x00020000);
+  if (a.stream_kv) {   // non-temporal: a launch whose K/V does not fit the caches (the last argument: nt)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&vr.v[wave][i * RPI][0], 16, (int)vdma_offset<D>(lane, i),
-                                             0, 0, 0);
+    for (int i = 0; i < D / 32; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&vr.v[wave][i * RPI][0], 16,
+                                               (int)vdma_offset<D>(lane, i), 0, 0, 2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&vr.v[wave][i * RPI][0], 16,
+                                               (int)vdma_offset<D>(lane, i), 0, 0, 0);
+  }
 }
 
 // One block b: V of the next block bn goes into the other buffer vn, K of the

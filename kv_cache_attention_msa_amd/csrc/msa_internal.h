@@ -83,6 +83,11 @@ struct Plan {
   // work-groups per CU) or 8 (256-row tiles, one per CU: half the K/V
   // staging per FLOP, for launches with at least two such tiles per CU).
   int32_t chunk_waves = 4;
+  // Per launch: 1 when its K/V blocks are streamed past the caches (non-
+  // temporal V staging in the decode kernel): a decode launch whose K/V
+  // exceeds twice the 256 MB Infinity Cache, so none of it would be found
+  // there again.  Smaller launches keep V cacheable.
+  int32_t stream_kv[3] = {0, 0, 0};
 };
 
 struct PlanConfig {
@@ -120,6 +125,7 @@ struct KernelArgs {
   int32_t causal;
   float scale_log2;       // scale * log2(e)
   int32_t max_mrows;      // largest n_q * group among the launch's items
+  int32_t stream_kv;      // 1: stage V with non-temporal loads (decode launches over large K/V)
   unsigned long long* trace;  // phase clocks of the chunk kernel (tracing builds only), or null
 };
 
