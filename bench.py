@@ -63,9 +63,12 @@ sys.path.insert(0, ROOT)
 METRIC = "MSA attention TFLOP/s (prefill) and HBM GB/s (decode) vs MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = {"prefill": "kv_cache_attention_msa_amd/csrc/msa_prefill.hip",
-                  "decode": "kv_cache_attention_msa_amd/csrc/msa_decode.hip",
-                  "write": "kv_cache_attention_msa_amd/csrc/msa_write.hip"}
+# the device sources each kernel is built from (a traffic record holds only while they are unchanged)
+KERNEL_SOURCES = {"prefill": ("kv_cache_attention_msa_amd/csrc/msa_prefill.hip",
+                              "kv_cache_attention_msa_amd/csrc/msa_decode_item.h"),
+                  "decode": ("kv_cache_attention_msa_amd/csrc/msa_decode.hip",
+                             "kv_cache_attention_msa_amd/csrc/msa_decode_item.h"),
+                  "write": ("kv_cache_attention_msa_amd/csrc/msa_write.hip",)}
 GATE_MFMA, GATE_HBM = 0.60, 0.70     # roofline fractions the benchmark definition asks for
 
 
@@ -100,9 +103,15 @@ def work_of(wl):
     return flops, kv_bytes + io_bytes
 
 
-def source_sha(rel):
-    p = os.path.join(ROOT, rel)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else None
+def source_sha(rels):
+    """sha256[:16] over the given source files, concatenated in order."""
+    h = hashlib.sha256()
+    for rel in rels:
+        p = os.path.join(ROOT, rel)
+        if not os.path.exists(p):
+            return None
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(kernel, units):
@@ -421,7 +430,8 @@ def write_report(args):
                   f"-> scale factors {kf:.3f} (fetch), {kw:.3f} (write)",
                   f"- scaled traffic per launch: {fetch_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written "
                   f"= {(fetch_b + write_b) / 1e6:.1f} MB",
-                  f"- kernel source sha256[:16]: {rec['kernel_src_sha']}"]
+                  f"- kernel sources ({', '.join(os.path.basename(r) for r in KERNEL_SOURCES[args.key])}) "
+                  f"sha256[:16]: {rec['kernel_src_sha']}"]
         with open(traffic_path(args.key, args.units), "w") as fh:
             json.dump(rec, fh, indent=1)
     if args.notes:
