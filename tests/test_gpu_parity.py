@@ -65,6 +65,21 @@ def test_random_bf16_eight_wave_chunk(seed):
     _check(wl, chunk_waves=4)
 
 
+def test_random_sweep():
+    """40 seeded small batches over the parameter space at once: GQA ratio,
+    head_dim, batch size, context and chunk lengths, decode share, forced KV
+    splits and the chunk work-group size, each against the oracle."""
+    rng = np.random.default_rng(2024)
+    groups = [(1, 1), (2, 1), (4, 1), (8, 2), (16, 2), (12, 4), (32, 8), (64, 8), (128, 1)]
+    for i in range(40):
+        hq, hkv = groups[int(rng.integers(len(groups)))]
+        d = int(rng.choice([64, 128]))
+        wl = W.random_case(300 + i, batch=int(rng.integers(1, 7)), H_q=hq, H_kv=hkv, d=d,
+                           max_ctx=int(rng.integers(16, 900)), max_chunk=int(rng.integers(1, 260)),
+                           decode_frac=float(rng.choice([0.0, 0.3, 0.7, 1.0])), qscale=float(rng.choice([0.5, 2.0])))
+        _check(wl, split_blocks=int(rng.choice([0, 0, 1, 3, 7])), chunk_waves=int(rng.choice([0, 4, 8])))
+
+
 def test_random_fp32_cases():
     for seed in range(3):
         _check(W.random_case(40 + seed, batch=3, H_q=4, H_kv=2, d=64, dtype="fp32"))
