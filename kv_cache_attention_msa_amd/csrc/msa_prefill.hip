@@ -16,8 +16,9 @@
 //   * then the next step's K and V go from the pool straight into the other
 //     LDS tile by LDS DMA (buffer loads with the lds flag, one buffer
 //     resource per pool block, whose 4 KiB per kv head are contiguous; each
-//     wave moves one block), so staging costs the waves neither registers
-//     nor LDS writes, and has the rest of the step to land;
+//     wave moves one block, or with 8 waves the K or the V of one), so staging
+//     costs the waves neither registers nor LDS writes, and has the rest of
+//     the step to land;
 //   * keys outside a block's valid slots, past the item's blocks, or (causal)
 //     at a position after the row's query position get score -inf by select;
 //     steps that are entirely visible to every row skip the mask;
