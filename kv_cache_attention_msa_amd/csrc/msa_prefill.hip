@@ -367,6 +367,9 @@ __device__ __forceinline__ void chunk_step(const KernelArgs& a, const WorkItem& 
   const float c2 = a.scale_log2;
 
   PHASE_START(pc);
+  // the compiler's interleaving of LDS reads with MFMAs (IGLP strategy 0)
+  // for the step: measured 0.3-1.2 % faster than its default schedule
+  __builtin_amdgcn_iglp_opt(0);
   // ---- S^T = K Q^T for 64 keys ----
   f32x16 s0 = (f32x16){0}, s1 = (f32x16){0};
 #pragma unroll
